@@ -1,0 +1,199 @@
+/*
+ * moe.h - C ABI of a single-GPU Mixture-of-Experts layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the MoE block of the DSV2-236B-MegaKernel README's flowchart
+ * ("What runs inside the single launch", stages N, O, P1/Q1, P2/Q2 and the
+ * sum of stage R), with every expert resident on the one GPU:
+ *
+ *   logits = x . Wr^T (+ bias)                          (stage N)
+ *   s      = softmax(logits) over all experts;           (stage O)
+ *            keep the topk_groups groups with the largest max member score,
+ *            take the topk experts of those groups, w = route_scale * s
+ *   dispatch of the T*topk (token, slot) pairs into per-expert segments
+ *            (Mixture-of-Kittens, Figure 1: GPU-side dispatch scheduling)
+ *   per expert e: h = SiLU(x.Wg_e^T) * (x.Wu_e^T); Y = h.Wd_e^T  (P1, P2)
+ *   shared expert S(x) on every token, unweighted       (Q1, Q2)
+ *   out    = bf16( sum_j w_j * Y_j + S )                 (stage R's sum,
+ *            without residual or norm)
+ *
+ * Conventions for every entry point
+ * - Pointers are device pointers unless marked (host).  bf16 tensors are
+ *   passed as uint16_t bit patterns.  All matrices are row-major with the
+ *   last index contiguous.  Device pointers must be 16-byte aligned.
+ * - Every call is asynchronous on `stream`; nothing synchronises with the
+ *   host and no device-side count is read back (Mixture-of-Kittens,
+ *   Abstract: no CPU-GPU synchronisation).  Launch errors are reported as
+ *   MOE_EHIP; faults inside kernels surface at the caller's next sync.
+ * - The caller owns all memory.  The library never allocates.  Calls that
+ *   take a workspace need `ws_bytes` >= moe_workspace_size(); the workspace
+ *   must be zero-filled once before its first use (torch.zeros is enough)
+ *   and is left reusable by every call.  Calls sharing one workspace must
+ *   be ordered on one stream.
+ * - Status codes: nothing is thrown across the ABI.  Host-side validation
+ *   runs before any launch, so a failed check launches nothing.
+ *     MOE_EINVAL        null pointer, T < 0, hidden/inter <= 0,
+ *                       n_experts % n_groups != 0, topk_groups not in
+ *                       [1, n_groups], topk not in [1, candidates], topk >
+ *                       16, route_scale not finite, bad format code
+ *     MOE_EALIGN        a pointer not 16-byte aligned, or hidden, inter or
+ *                       shared_inter not a multiple of 128
+ *     MOE_EUNSUPPORTED  n_experts > 256, n_groups > 64, or a weight /
+ *                       activation format pair that no kernel implements
+ *     MOE_EWORKSPACE    ws_bytes below moe_workspace_size()
+ *     MOE_EHIP          a HIP launch failed
+ *   T = 0 is a no-op returning MOE_OK.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EALIGN = 3,
+  MOE_EWORKSPACE = 4,
+  MOE_EHIP = 5
+} moe_status;
+
+/* Weight formats (DSV2-236B-MegaKernel README, "Results": per-128
+ * block-scaled FP8; Mixture-of-Kittens, Table 2: MXFP8 routed experts and a
+ * BF16 shared expert).  For a weight matrix W[N][K]:
+ *   MOE_W_BF16      W bf16 [N][K], no scales
+ *   MOE_W_FP8_B128  codes e4m3fn u8 [N][K] and fp32 scales [N/128][K/128];
+ *                   W[n][k] = dec(q[n][k]) * S[n/128][k/128]
+ *   MOE_W_MXFP8     codes e4m3fn u8 [N][K] and e8m0 u8 scales [N][K/32];
+ *                   W[n][k] = dec(q[n][k]) * 2^(E[n][k/32] - 127)          */
+typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_B128 = 1, MOE_W_MXFP8 = 2 } moe_wfmt;
+
+/* Activation formats: how the rows entering each FFN matmul (x, then h) are
+ * quantised ("From 35 to 873 tokens/s", Rounds 12-15: MXFP8 quantisation of
+ * the expert inputs).  Per row:
+ *   MOE_A_NONE        bf16 x as given; h kept in fp32 (bf16 for bf16 weights)
+ *   MOE_A_FP8_1X128   per 128 columns: s = fl32(amax/448) (1 if amax = 0),
+ *                     q = RNE_e4m3(fl32(v/s)) saturating; scales fp32
+ *                     [rows][cols/128]
+ *   MOE_A_MXFP8_1X32  per 32 columns: X = 2^(floor(log2 amax) - 8) clamped to
+ *                     the e8m0 range (1 if amax = 0), q = RNE_e4m3(v/X)
+ *                     saturating; scales e8m0 u8 [rows][cols/32]
+ * Supported (weight, activation) pairs: (BF16, NONE), (FP8_B128, NONE),
+ * (FP8_B128, FP8_1X128), (MXFP8, MXFP8_1X32), (MXFP8, NONE).  Pairs with
+ * activation NONE and FP8/MXFP8 weights run on the small-batch GEMV path
+ * at any T (slow for large T).                                              */
+typedef enum { MOE_A_NONE = 0, MOE_A_FP8_1X128 = 1, MOE_A_MXFP8_1X32 = 2 } moe_afmt;
+
+/* Layer geometry and formats (host struct).  Experts are grouped into
+ * n_groups contiguous id ranges of n_experts/n_groups (stage O's
+ * "8 groups x 20").  shared_inter = 0 means no shared expert. */
+typedef struct {
+  int32_t hidden;        /* H */
+  int32_t n_experts;     /* E <= 256 */
+  int32_t n_groups;      /* G, divides E */
+  int32_t topk_groups;   /* TG in [1, G] */
+  int32_t topk;          /* K in [1, min(16, TG*E/G)] */
+  int32_t inter;         /* I, routed expert intermediate */
+  int32_t shared_inter;  /* Is, fused shared intermediate, 0 = none */
+  float route_scale;     /* w = route_scale * softmax score */
+  int32_t routed_wfmt;   /* moe_wfmt */
+  int32_t shared_wfmt;   /* moe_wfmt */
+  int32_t routed_afmt;   /* moe_afmt */
+  int32_t shared_afmt;   /* moe_afmt */
+} moe_config;
+
+/* One set of expert weights (device pointers).  gate, up: [n][I][H];
+ * down: [n][H][I]; n = E for routed, 1 for shared.  Scales per moe_wfmt
+ * with the same leading [n]; NULL for BF16. */
+typedef struct {
+  const void* gate;
+  const void* up;
+  const void* down;
+  const void* gate_s;
+  const void* up_s;
+  const void* down_s;
+} moe_ffn_weights;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int32_t status);
+
+/* Bytes of workspace that every call below needs for up to max_tokens
+ * tokens with this config.  Host-only; no GPU work. */
+moe_status moe_workspace_size(const moe_config* cfg /*host*/, int32_t max_tokens,
+                              size_t* bytes /*host*/);
+
+/* Stages N + O: router GEMV and group-limited greedy top-k.
+ * x bf16 [T][H]; w_router bf16 [E][H]; bias fp32 [E] or NULL (added to the
+ * logits before the softmax).  Outputs topk_ids int32 [T][K] in descending
+ * score order (ties to the lower id) and topk_w fp32 [T][K] =
+ * route_scale * score (no renormalisation over the selected experts). */
+moe_status moe_route(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
+                     const uint16_t* w_router, const float* bias, int32_t* topk_ids,
+                     float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch (Mixture-of-Kittens, Figure 1: dispatch scheduling on the GPU;
+ * "From 35 to 873 tokens/s", Rounds 12-15: the router emits the layout the
+ * experts need).  Flat slot p = t*K + j.  Outputs:
+ *   expert_offsets int32 [E+1]: exclusive prefix sum of per-expert counts
+ *   perm_src int32 [T*K]: slot held by permuted row pos, stable (expert
+ *            ascending, then p ascending)
+ *   inv_pos int32 [T*K]: permuted row of slot p (-1 if its id is outside
+ *            [0, E); such slots are dropped)
+ *   x_perm (optional, NULL to skip; needs x): row pos = x[perm_src[pos]/K]
+ *            in the routed activation format: bf16 [T*K][H] for NONE, else
+ *            e4m3 codes u8 [T*K][H] with scales written to x_perm_scale
+ *            (fp32 [T*K][H/128] or e8m0 u8 [T*K][H/32]). */
+moe_status moe_permute(const moe_config* cfg /*host*/, const int32_t* topk_ids, int32_t T,
+                       const uint16_t* x, int32_t* expert_offsets, int32_t* perm_src,
+                       int32_t* inv_pos, void* x_perm, void* x_perm_scale, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Stages P1+P2 (which = 0, routed) or Q1+Q2 (which = 1, shared): the SwiGLU
+ * FFN y = (SiLU(x.Wg^T) * (x.Wu^T)).Wd^T on `rows` rows.
+ *   x: bf16 [rows][H] when x_scale is NULL (quantised here per the afmt),
+ *      else e4m3 codes u8 [rows][H] already quantised with x_scale in the
+ *      afmt's scale layout.
+ *   seg_offsets: routed only, int32 [E+1] device array splitting the rows
+ *      into per-expert segments (as written by moe_permute); NULL for shared.
+ *   y: fp32 [rows][H], unweighted. */
+moe_status moe_expert_ffn(const moe_config* cfg /*host*/, int32_t which, const void* x,
+                          const void* x_scale, int32_t rows, const int32_t* seg_offsets,
+                          const moe_ffn_weights* weights /*host struct, device ptrs*/,
+                          float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage R's sum, deterministic (a fixed order, no float atomics):
+ * out[t] = bf16( sum_{j=0..K-1} topk_w[t][j] * y_perm[inv_pos[t*K+j]]
+ *                + y_shared[t] ).
+ * y_perm fp32 [T*K][H]; inv_pos int32 [T*K] (-1 entries are skipped);
+ * topk_w fp32 [T][K]; y_shared fp32 [T][H] or NULL; out bf16 [T][H]. */
+moe_status moe_combine(const moe_config* cfg /*host*/, const float* y_perm, const int32_t* inv_pos,
+                       const float* topk_w, const float* y_shared, int32_t T, uint16_t* out,
+                       hipStream_t stream);
+
+/* The whole layer: route, dispatch, routed and shared FFNs, combine.
+ * out bf16 [T][H].  topk_ids_out int32 [T][K] and topk_w_out fp32 [T][K]
+ * may be NULL.  Numerics depend only on cfg: every path honours the same
+ * activation format. */
+moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
+                       const uint16_t* w_router, const float* bias,
+                       const moe_ffn_weights* routed /*host struct*/,
+                       const moe_ffn_weights* shared /*host struct or NULL*/, uint16_t* out,
+                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Diagnostics of the device FP8 codec (the conversions every kernel uses):
+ * decode n e4m3 codes to fp32, and encode n fp32 values with the library's
+ * round-to-nearest-even saturating rule.  For tests of the codec itself. */
+moe_status moe_debug_e4m3_decode(const uint8_t* codes, float* out, int32_t n, hipStream_t stream);
+moe_status moe_debug_e4m3_encode(const float* in, uint8_t* codes, int32_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,547 @@
+// C ABI of the MoE layer library: host-side validation, workspace planning,
+// path selection and kernel orchestration.  Declarations and the contract of
+// every entry point are in include/moe.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kGemvMaxT = 4;       // moe_forward: T <= this runs the GEMV path
+constexpr int kGemvMaxRows = 16;   // moe_expert_ffn: rows <= this runs the GEMV path
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// test hook: MOE_FORCE_PATH=gemv|gemm
+int forced_path() {
+  const char* s = getenv("MOE_FORCE_PATH");
+  if (!s) return 0;
+  if (!strcmp(s, "gemv")) return 1;
+  if (!strcmp(s, "gemm")) return 2;
+  return 0;
+}
+
+bool gemm_pair(int wf, int af) {
+  return (wf == W_BF16 && af == A_NONE) || (wf == W_FP8_B128 && af == A_FP8_1X128) ||
+         (wf == W_MXFP8 && af == A_MXFP8_1X32);
+}
+bool any_pair(int wf, int af) {
+  return gemm_pair(wf, af) || (wf == W_FP8_B128 && af == A_NONE) || (wf == W_MXFP8 && af == A_NONE);
+}
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->hidden <= 0 || c->inter <= 0 || c->shared_inter < 0 || c->n_experts <= 0 || c->n_groups <= 0)
+    return MOE_EINVAL;
+  if (c->n_experts % c->n_groups != 0) return MOE_EINVAL;
+  if (c->topk_groups < 1 || c->topk_groups > c->n_groups) return MOE_EINVAL;
+  const int cand = c->topk_groups * (c->n_experts / c->n_groups);
+  if (c->topk < 1 || c->topk > cand || c->topk > 16) return MOE_EINVAL;
+  if (!isfinite(c->route_scale)) return MOE_EINVAL;
+  for (int f : {c->routed_wfmt, c->shared_wfmt})
+    if (f < 0 || f > 2) return MOE_EINVAL;
+  for (int f : {c->routed_afmt, c->shared_afmt})
+    if (f < 0 || f > 2) return MOE_EINVAL;
+  if (c->n_experts > 256 || c->n_groups > 64) return MOE_EUNSUPPORTED;
+  if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128) return MOE_EALIGN;
+  if (!any_pair(c->routed_wfmt, c->routed_afmt)) return MOE_EUNSUPPORTED;
+  if (c->shared_inter > 0 && !any_pair(c->shared_wfmt, c->shared_afmt)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_ffn_weights* w, int wfmt) {
+  if (!w || !w->gate || !w->up || !w->down) return MOE_EINVAL;
+  if (wfmt != W_BF16 && (!w->gate_s || !w->up_s || !w->down_s)) return MOE_EINVAL;
+  for (const void* p : {w->gate, w->up, w->down})
+    if (!aligned16(p)) return MOE_EALIGN;
+  if (wfmt != W_BF16)
+    for (const void* p : {w->gate_s, w->up_s, w->down_s})
+      if (!aligned16(p)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+size_t act_scale_bytes(int afmt, size_t rows, int cols) {
+  if (afmt == A_FP8_1X128) return rows * (cols / 128) * 4;
+  if (afmt == A_MXFP8_1X32) return rows * (cols / 32);
+  return 0;
+}
+// bytes of an activation matrix [rows][cols] in the GEMM path
+size_t act_bytes(int afmt, size_t rows, int cols) {
+  return afmt == A_NONE ? rows * cols * 2 : rows * cols;
+}
+size_t wscale_stride(int wfmt, int N, int K) {  // scale elements per expert
+  if (wfmt == W_FP8_B128) return size_t(N / 128) * (K / 128);
+  if (wfmt == W_MXFP8) return size_t(N) * (K / 32);
+  return 0;
+}
+
+struct Ws {
+  size_t counter, logits, ids, w, offsets, perm, inv, tiles, ntiles;
+  size_t xq, xqs, xs2, xs2s;  // routed-format x, shared-format x
+  size_t h, hs, hsh, hshs;    // routed h (+scales), shared h (+scales)
+  size_t yperm, ysh;
+  size_t total;
+};
+
+Ws plan(const moe_config* c, int Tm) {
+  const size_t T = size_t(std::max(Tm, 1)), K = c->topk, E = c->n_experts, H = c->hidden, I = c->inter,
+               Is = c->shared_inter;
+  const size_t TK = T * K;
+  Ws s{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up(std::max<size_t>(bytes, 16));
+    return at;
+  };
+  s.counter = take(256);
+  s.logits = take(T * E * 4);
+  s.ids = take(TK * 4);
+  s.w = take(TK * 4);
+  s.offsets = take((E + 1) * 4);
+  s.perm = take(TK * 4);
+  s.inv = take(TK * 4);
+  s.tiles = take(size_t(2) * max_tiles(int(TK), int(E), kGemmBM) * 4);
+  s.ntiles = take(16);
+  // x in the routed activation format: quantised rows (up to TK rows for
+  // moe_expert_ffn) or fp32 dequantised rows for the GEMV path
+  s.xq = take(TK * H * 4);
+  s.xqs = take(std::max(act_scale_bytes(A_FP8_1X128, TK, int(H)), act_scale_bytes(A_MXFP8_1X32, TK, int(H))));
+  s.xs2 = take(T * H * 4);
+  s.xs2s = take(std::max(act_scale_bytes(A_FP8_1X128, T, int(H)), act_scale_bytes(A_MXFP8_1X32, T, int(H))));
+  s.h = take(TK * I * 4);
+  s.hs = take(std::max(act_scale_bytes(A_FP8_1X128, TK, int(I)), act_scale_bytes(A_MXFP8_1X32, TK, int(I))));
+  if (Is) {
+    s.hsh = take(T * Is * 4);
+    s.hshs = take(std::max(act_scale_bytes(A_FP8_1X128, T, int(Is)), act_scale_bytes(A_MXFP8_1X32, T, int(Is))));
+    s.ysh = take(T * H * 4);
+  }
+  s.yperm = take(TK * H * 2);
+  s.total = o;
+  return s;
+}
+
+template <class P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<uint8_t*>(ws) + off);
+}
+
+RouteParams route_params(const moe_config* c) {
+  return RouteParams{c->hidden, c->n_experts, c->n_groups, c->topk_groups, c->topk, c->route_scale};
+}
+
+#define HIP_TRY(expr)                             \
+  do {                                            \
+    if ((expr) != hipSuccess) return MOE_EHIP;    \
+  } while (0)
+
+moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_t* wr, const float* bias, int* ids,
+                    float* w, void* ws, const Ws& L, hipStream_t s) {
+  const RouteParams rp = route_params(c);
+  if (T <= kRouteGemvMaxT) {
+    HIP_TRY(launch_route_gemv_topk(x, T, wr, bias, rp, at<float>(ws, L.logits), at<unsigned>(ws, L.counter), ids, w,
+                                   s));
+    return MOE_OK;
+  }
+  GemmParams g{};
+  g.A = x;
+  g.lda = c->hidden;
+  g.B0 = wr;
+  g.N = c->n_experts;
+  g.K = c->hidden;
+  g.M = T;
+  g.C = at<float>(ws, L.logits);
+  g.ldc = c->n_experts;
+  HIP_TRY(launch_gemm(W_BF16, EPI_F32, g, s));
+  HIP_TRY(launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s));
+  return MOE_OK;
+}
+
+// GEMM-path FFN on rows already laid out per segment (or all rows for the
+// shared expert).  A: activation rows in `afmt` (bf16 when A_NONE); a_map
+// gathers rows.  Output: y (fp32 or bf16) [rows][H].
+moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void* As, const int* a_map, int a_div,
+                    int rows, const int* seg, const int* tiles, const int* ntiles, int maxt,
+                    const moe_ffn_weights* W, void* h, void* hs, void* y, bool y_bf16, hipStream_t s) {
+  const int wf = routed ? c->routed_wfmt : c->shared_wfmt;
+  const int af = routed ? c->routed_afmt : c->shared_afmt;
+  const int I = routed ? c->inter : c->shared_inter;
+  const int H = c->hidden;
+  GemmParams g{};
+  g.A = A;
+  g.lda = H;
+  g.As = As;
+  g.a_map = a_map;
+  g.a_div = a_div;
+  g.B0 = W->gate;
+  g.B1 = W->up;
+  g.b_stride = long(I) * H;
+  g.B0s = W->gate_s;
+  g.B1s = W->up_s;
+  g.bs_stride = long(wscale_stride(wf, I, H));
+  g.N = I;
+  g.K = H;
+  g.seg = seg;
+  g.M = rows;
+  g.tiles = tiles;
+  g.ntiles = ntiles;
+  g.max_tiles = maxt;
+  g.C = h;
+  g.ldc = I;
+  g.Cs = hs;
+  g.out_afmt = af;
+  HIP_TRY(launch_gemm(wf, EPI_GATEUP, g, s));
+  GemmParams d{};
+  d.A = h;
+  d.lda = I;
+  d.As = hs;
+  d.B0 = W->down;
+  d.b_stride = long(H) * I;
+  d.B0s = W->down_s;
+  d.bs_stride = long(wscale_stride(wf, H, I));
+  d.N = H;
+  d.K = I;
+  d.seg = seg;
+  d.M = rows;
+  d.tiles = tiles;
+  d.ntiles = ntiles;
+  d.max_tiles = maxt;
+  d.C = y;
+  d.ldc = H;
+  HIP_TRY(launch_gemm(wf, y_bf16 ? EPI_BF16 : EPI_F32, d, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: configuration not implemented";
+    case MOE_EALIGN: return "MOE_EALIGN: pointer or dimension misaligned";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes) {
+  if (!bytes || max_tokens < 0) return MOE_EINVAL;
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  *bytes = plan(cfg, max_tokens).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router, const float* bias,
+                     int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w || !ws) return MOE_EINVAL;
+  for (const void* p : {(const void*)x, (const void*)w_router, (const void*)ws})
+    if (!aligned16(p)) return MOE_EALIGN;
+  const Ws L = plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  return do_route(cfg, x, T, w_router, bias, topk_ids, topk_w, ws, L, stream);
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T, const uint16_t* x,
+                       int32_t* expert_offsets, int32_t* perm_src, int32_t* inv_pos, void* x_perm,
+                       void* x_perm_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !expert_offsets || !perm_src || !inv_pos || !ws) return MOE_EINVAL;
+  if (x_perm && !x) return MOE_EINVAL;
+  if (x_perm && cfg->routed_afmt != A_NONE && !x_perm_scale) return MOE_EINVAL;
+  if (!aligned16(ws) || (x && !aligned16(x)) || (x_perm && !aligned16(x_perm))) return MOE_EALIGN;
+  const Ws L = plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const int TK = T * cfg->topk;
+  HIP_TRY(launch_permute(topk_ids, TK, cfg->n_experts, expert_offsets, perm_src, inv_pos, nullptr, nullptr, kGemmBM,
+                         stream));
+  if (x_perm)
+    HIP_TRY(launch_quant_rows(x, false, TK, cfg->hidden, perm_src, cfg->topk, cfg->routed_afmt, x_perm, x_perm_scale,
+                              nullptr, stream));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, const void* x_scale, int32_t rows,
+                          const int32_t* seg_offsets, const moe_ffn_weights* W, float* y, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (which != 0 && which != 1) return MOE_EINVAL;
+  const bool routed = which == 0;
+  if (!routed && cfg->shared_inter == 0) return MOE_EINVAL;
+  if (rows < 0) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!x || !W || !y || !ws || (routed && !seg_offsets)) return MOE_EINVAL;
+  const int wf = routed ? cfg->routed_wfmt : cfg->shared_wfmt;
+  const int af = routed ? cfg->routed_afmt : cfg->shared_afmt;
+  if ((st = check_weights(W, wf)) != MOE_OK) return st;
+  if (x_scale && af == A_NONE) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws) || (x_scale && !aligned16(x_scale))) return MOE_EALIGN;
+  // rows <= max_tokens*K for routed, <= max_tokens for shared: size the plan accordingly
+  const int Tm = routed ? (rows + cfg->topk - 1) / cfg->topk : rows;
+  const Ws L = plan(cfg, Tm);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const int H = cfg->hidden, I = routed ? cfg->inter : cfg->shared_inter, E = cfg->n_experts;
+  const int fp = forced_path();
+  const bool gemv = fp == 1 || (fp != 2 && rows <= kGemvMaxRows) || !gemm_pair(wf, af);
+  if (fp == 2 && !gemm_pair(wf, af)) return MOE_EUNSUPPORTED;
+
+  if (gemv) {
+    const void* xin = x;
+    bool xf32 = false;
+    if (x_scale) {  // pre-quantised rows: dequantise to fp32
+      HIP_TRY(launch_dequant_rows(static_cast<const uint8_t*>(x), x_scale, af, rows, H, at<float>(ws, L.xq), stream));
+      xin = at<float>(ws, L.xq);
+      xf32 = true;
+    } else if (af != A_NONE) {
+      HIP_TRY(launch_quant_rows(x, false, rows, H, nullptr, 1, af, nullptr, nullptr, at<float>(ws, L.xq), stream));
+      xin = at<float>(ws, L.xq);
+      xf32 = true;
+    }
+    float* h = at<float>(ws, routed ? L.h : L.hsh);
+    GemvUpParams u{};
+    u.T = rows;
+    u.H = H;
+    u.E = E;
+    if (routed) {
+      u.wfmt = wf;
+      u.swfmt = wf;
+      u.x = xin;
+      u.x_f32 = xf32;
+      u.seg = seg_offsets;
+      u.g = W->gate; u.u = W->up; u.gs = W->gate_s; u.us = W->up_s;
+      u.I = I;
+      u.h = h;
+    } else {
+      u.wfmt = wf;
+      u.swfmt = wf;
+      u.xs = xin;
+      u.xs_f32 = xf32;
+      u.sg = W->gate; u.su = W->up; u.sgs = W->gate_s; u.sus = W->up_s;
+      u.Is = I;
+      u.I = 128;
+      u.hs = h;
+    }
+    HIP_TRY(launch_gemv_gate_up(u, stream));
+    if (af != A_NONE) HIP_TRY(launch_quant_rows(h, true, rows, I, nullptr, 1, af, nullptr, nullptr, h, stream));
+    GemvDownParams d{};
+    d.wfmt = wf;
+    d.swfmt = wf;
+    d.H = H;
+    d.rows = rows;
+    d.y = y;
+    d.E = E;
+    if (routed) {
+      d.I = I; d.h = h; d.d = W->down; d.ds = W->down_s; d.seg = seg_offsets;
+    } else {
+      d.Is = I; d.hs = h; d.sd = W->down; d.sds = W->down_s;
+    }
+    HIP_TRY(launch_gemv_down(d, stream));
+    return MOE_OK;
+  }
+
+  // GEMM path
+  const void* A = x;
+  const void* As = x_scale;
+  if (!x_scale && af != A_NONE) {
+    HIP_TRY(launch_quant_rows(x, false, rows, H, nullptr, 1, af, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
+                              stream));
+    A = at<void>(ws, L.xq);
+    As = at<void>(ws, L.xqs);
+  }
+  int* tiles = nullptr;
+  int* ntiles = nullptr;
+  int maxt = 0;
+  if (routed) {
+    tiles = at<int>(ws, L.tiles);
+    ntiles = at<int>(ws, L.ntiles);
+    maxt = max_tiles(rows, E, kGemmBM);
+    HIP_TRY(launch_build_tiles(seg_offsets, E, rows, kGemmBM, tiles, ntiles, stream));
+  }
+  return gemm_ffn(cfg, routed, A, As, nullptr, 1, rows, routed ? seg_offsets : nullptr, tiles, ntiles, maxt, W,
+                  at<void>(ws, routed ? L.h : L.hsh), at<void>(ws, routed ? L.hs : L.hshs), y, false, stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* inv_pos, const float* topk_w,
+                       const float* y_shared, int32_t T, uint16_t* out, hipStream_t stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !inv_pos || !topk_w || !out) return MOE_EINVAL;
+  if (!aligned16(y_perm) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_EALIGN;
+  HIP_TRY(launch_combine(y_perm, false, inv_pos, topk_w, y_shared, false, T, cfg->topk, cfg->hidden, out, stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
+                       const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared, uint16_t* out,
+                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !routed || !out || !ws) return MOE_EINVAL;
+  const bool has_shared = cfg->shared_inter > 0;
+  if (has_shared && !shared) return MOE_EINVAL;
+  if ((st = check_weights(routed, cfg->routed_wfmt)) != MOE_OK) return st;
+  if (has_shared && (st = check_weights(shared, cfg->shared_wfmt)) != MOE_OK) return st;
+  for (const void* p : {(const void*)x, (const void*)w_router, (const void*)out, (const void*)ws})
+    if (!aligned16(p)) return MOE_EALIGN;
+  const Ws L = plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+
+  const int H = cfg->hidden, K = cfg->topk, E = cfg->n_experts, TK = T * K;
+  const int raf = cfg->routed_afmt, saf = cfg->shared_afmt;
+  int* ids = topk_ids_out ? topk_ids_out : at<int>(ws, L.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  const int fp = forced_path();
+  const bool pairs_ok = gemm_pair(cfg->routed_wfmt, raf) && (!has_shared || gemm_pair(cfg->shared_wfmt, saf));
+  if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
+  const bool gemv = fp == 1 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
+
+  if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
+
+  if (gemv) {
+    const void* xr = x;
+    bool xr32 = false;
+    if (raf != A_NONE) {
+      HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
+      xr = at<float>(ws, L.xq);
+      xr32 = true;
+    }
+    const void* xs = x;
+    bool xs32 = false;
+    if (has_shared && saf != A_NONE) {
+      if (saf == raf) {
+        xs = xr;
+      } else {
+        HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
+        xs = at<float>(ws, L.xs2);
+      }
+      xs32 = true;
+    }
+    float* h = at<float>(ws, L.h);
+    float* hs = has_shared ? at<float>(ws, L.hsh) : nullptr;
+    GemvUpParams u{};
+    u.wfmt = cfg->routed_wfmt;
+    u.swfmt = has_shared ? cfg->shared_wfmt : cfg->routed_wfmt;
+    u.x = xr;
+    u.x_f32 = xr32;
+    u.T = T;
+    u.H = H;
+    u.ids = ids;
+    u.K = K;
+    u.g = routed->gate; u.u = routed->up; u.gs = routed->gate_s; u.us = routed->up_s;
+    u.I = cfg->inter;
+    u.h = h;
+    if (has_shared) {
+      u.sg = shared->gate; u.su = shared->up; u.sgs = shared->gate_s; u.sus = shared->up_s;
+      u.Is = cfg->shared_inter;
+      u.hs = hs;
+      u.xs = xs;
+      u.xs_f32 = xs32;
+    }
+    u.E = E;
+    HIP_TRY(launch_gemv_gate_up(u, stream));
+    if (raf != A_NONE) HIP_TRY(launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
+    if (has_shared && saf != A_NONE)
+      HIP_TRY(launch_quant_rows(hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, hs, stream));
+    GemvDownParams d{};
+    d.wfmt = cfg->routed_wfmt;
+    d.swfmt = u.swfmt;
+    d.T = T;
+    d.H = H;
+    d.K = K;
+    d.I = cfg->inter;
+    d.Is = cfg->shared_inter;
+    d.ids = ids;
+    d.w = w;
+    d.h = h;
+    d.hs = hs;
+    d.d = routed->down; d.ds = routed->down_s;
+    if (has_shared) { d.sd = shared->down; d.sds = shared->down_s; }
+    d.out = out;
+    d.E = E;
+    HIP_TRY(launch_gemv_down(d, stream));
+    return MOE_OK;
+  }
+
+  // batched path
+  int* off = at<int>(ws, L.offsets);
+  int* perm = at<int>(ws, L.perm);
+  int* inv = at<int>(ws, L.inv);
+  int* tiles = at<int>(ws, L.tiles);
+  int* ntiles = at<int>(ws, L.ntiles);
+  HIP_TRY(launch_permute(ids, TK, E, off, perm, inv, tiles, ntiles, kGemmBM, stream));
+  const void* xa = x;
+  const void* xas = nullptr;
+  if (raf != A_NONE) {
+    HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, raf, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
+                              stream));
+    xa = at<void>(ws, L.xq);
+    xas = at<void>(ws, L.xqs);
+  }
+  if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, kGemmBM), routed,
+                     at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
+    return st;
+  float* ysh = nullptr;
+  if (has_shared) {
+    const void* xs = x;
+    const void* xss = nullptr;
+    if (saf != A_NONE) {
+      if (saf == raf) {
+        xs = xa;
+        xss = xas;
+      } else {
+        HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
+                                  nullptr, stream));
+        xs = at<void>(ws, L.xs2);
+        xss = at<void>(ws, L.xs2s);
+      }
+    }
+    ysh = at<float>(ws, L.ysh);
+    if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0, shared, at<void>(ws, L.hsh),
+                       at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
+      return st;
+  }
+  HIP_TRY(launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
+  return MOE_OK;
+}
+
+moe_status moe_debug_e4m3_decode(const uint8_t* codes, float* out, int32_t n, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!codes || !out))) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  HIP_TRY(launch_e4m3_decode(codes, out, n, stream));
+  return MOE_OK;
+}
+
+moe_status moe_debug_e4m3_encode(const float* in, uint8_t* codes, int32_t n, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!codes || !in))) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  HIP_TRY(launch_e4m3_encode(in, codes, n, stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Host-side launchers of the gfx950 kernels (internal interface between the
+// C ABI in api.hip and the kernel translation units).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum WFmt { W_BF16 = 0, W_FP8_B128 = 1, W_MXFP8 = 2 };
+enum AFmt { A_NONE = 0, A_FP8_1X128 = 1, A_MXFP8_1X32 = 2 };
+
+// ------------------------------------------------------------------ routing
+struct RouteParams {
+  int H, E, G, TG, K;
+  float scale;
+};
+// Small-T router: GEMV over the E rows spread over the grid, then the last
+// workgroup to finish runs the top-k for every token.  T <= kRouteGemvMaxT.
+constexpr int kRouteGemvMaxT = 4;
+hipError_t launch_route_gemv_topk(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
+                                  const RouteParams& p, float* logits_ws, unsigned* counter_ws,
+                                  int* ids, float* w, hipStream_t s);
+// Top-k over precomputed fp32 logits [T][E] (bias added here).
+hipError_t launch_topk(const float* logits, int T, const float* bias, const RouteParams& p, int* ids,
+                       float* w, hipStream_t s);
+
+// ------------------------------------------------------------------ dispatch
+// ids [TK]; writes offsets [E+1], perm_src [TK], inv_pos [TK]; when tiles is
+// non-null also the grouped-GEMM tile list for row tiles of `bm` rows:
+// tiles[2i] = expert, tiles[2i+1] = row offset in the segment; ntiles[0] = count.
+hipError_t launch_permute(const int* ids, int TK, int E, int* offsets, int* perm_src, int* inv_pos,
+                          int* tiles, int* ntiles, int bm, hipStream_t s);
+hipError_t launch_build_tiles(const int* offsets, int E, int rows, int bm, int* tiles, int* ntiles, hipStream_t s);
+inline int max_tiles(int rows, int E, int bm) { return (rows + bm - 1) / bm + E; }
+
+// ------------------------------------------------------------------ quantisers
+// Row r of the output reads input row (row_map ? row_map[r] / row_div : r).
+// in: bf16 (in_f32 = false) or fp32.  Modes:
+//   A_NONE: copy as bf16 to q (as uint16) [rows][H]
+//   A_FP8_1X128 / A_MXFP8_1X32: codes u8 to q, scales to qs
+// When deq_out is non-null the dequantised values (code * scale, or the
+// bf16/fp32 value itself for A_NONE) are written there as fp32 instead.
+hipError_t launch_quant_rows(const void* in, bool in_f32, int rows, int H, const int* row_map, int row_div,
+                             int afmt, void* q, void* qs, float* deq_out, hipStream_t s);
+
+// codes u8 [rows][H] + scales (afmt layout) -> fp32 code * scale
+hipError_t launch_dequant_rows(const uint8_t* q, const void* qs, int afmt, int rows, int H, float* out, hipStream_t s);
+
+// ------------------------------------------------------------------ grouped GEMM (MFMA)
+enum Epi { EPI_F32 = 0, EPI_BF16 = 1, EPI_GATEUP = 2 };
+struct GemmParams {
+  // A: rows of K elements; bf16 for W_BF16, e4m3 codes otherwise
+  const void* A;
+  long lda;          // elements
+  const void* As;    // A scales (fp32 [rows][K/128] or e8m0 [rows][K/32]); null for bf16
+  const int* a_map;  // optional gather: physical row = a_map[r] / a_div
+  int a_div;
+  // B: per group [N][K] (gate in B0, up in B1 for EPI_GATEUP)
+  const void* B0;
+  const void* B1;
+  long b_stride;  // elements per group
+  const void* B0s;
+  const void* B1s;
+  long bs_stride;  // scale elements per group
+  int N;           // output columns (h columns for EPI_GATEUP)
+  int K;
+  // rows: segments seg[g]..seg[g+1] (seg null: one group of M rows)
+  const int* seg;
+  int M;
+  const int* tiles;  // device tile list (null: tiles are 0..ceil(M/BM)-1 of group 0)
+  const int* ntiles;
+  int max_tiles;
+  // output
+  void* C;
+  long ldc;
+  void* Cs;       // scales of quantised h (EPI_GATEUP with out_afmt != A_NONE)
+  int out_afmt;   // EPI_GATEUP: A_NONE -> bf16 h; else quantised h
+  float* C_f32;   // EPI_GATEUP only: if non-null, h is written as fp32 here instead
+};
+constexpr int kGemmBM = 64;
+hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ small-batch GEMV FFN
+struct GemvUpParams {
+  int wfmt;
+  const void* x;      // bf16 [T][H] (x_f32 false) or fp32 dequantised [T][H]
+  bool x_f32;
+  int T, H;
+  // routed slots (T*K of them): expert = ids[slot], token = slot / K
+  const int* ids;     // null: no routed slots
+  int K;
+  const void *g, *u, *gs, *us;  // routed weights
+  int I;
+  float* h;           // fp32 [T*K][I]
+  // shared expert on every token
+  const void *sg, *su, *sgs, *sus;
+  int swfmt;
+  int Is;
+  float* hs;          // fp32 [T][Is]
+  const void* xs;     // x for the shared expert (may differ in quantisation)
+  bool xs_f32;
+  // per-slot rows when the routed slots are "rows" of an explicit segment
+  // list (moe_expert_ffn): expert of row r from seg; token = r
+  const int* seg;
+  int E;
+};
+hipError_t launch_gemv_gate_up(const GemvUpParams& p, hipStream_t s);
+
+struct GemvDownParams {
+  int wfmt, swfmt;
+  int T, H, K, I, Is;
+  const int* ids;      // [T][K] experts (null: only the shared part / explicit seg mode)
+  const float* w;      // [T][K] routing weights (combine mode)
+  const float* h;      // fp32 [T*K][I] (routed)
+  const float* hs;     // fp32 [T][Is] (shared) or null
+  const void *d, *ds;  // routed down [E][H][I] + scales
+  const void *sd, *sds;
+  // combine mode: out bf16 [T][H] = sum_j w*Y_j + S.  Per-row mode (out null):
+  // y fp32 [rows][H] = h_row . Wd_e, expert from seg (or shared when seg null
+  // and ids null)
+  uint16_t* out;
+  float* y;
+  int rows;
+  const int* seg;
+  int E;
+};
+hipError_t launch_gemv_down(const GemvDownParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ combine
+// out[t] = bf16(sum_j w[t][j] * y_perm[inv_pos[t*K+j]] + y_shared[t]).
+hipError_t launch_combine(const void* y_perm, bool y_bf16, const int* inv_pos, const float* w,
+                          const void* y_shared, bool ys_bf16, int T, int K, int H, uint16_t* out,
+                          hipStream_t s);
+
+// ------------------------------------------------------------------ diagnostics
+hipError_t launch_e4m3_decode(const uint8_t* codes, float* out, int n, hipStream_t s);
+hipError_t launch_e4m3_encode(const float* in, uint8_t* codes, int n, hipStream_t s);
+
+}  // namespace moe

@@ -26,5 +26,5 @@ routines, closed forms, brute force, invariants).
 from .fp8 import e4m3_decode, e4m3_encode, e8m0_decode  # noqa: F401
 from .moe import (  # noqa: F401
     bf16_to_f64, dequant_weight, quant_act, route, route_margins, permute,
-    expert_ffn, forward, forward_tokens, forward_dense_masked, OracleResult,
+    expert_ffn, combine, forward, forward_tokens, forward_dense_masked, OracleResult,
 )

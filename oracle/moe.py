@@ -66,14 +66,18 @@ def dequant_weight(codes, scales, fmt):
     """
     if fmt == "bf16":
         return bf16_to_f64(codes)
-    q = e4m3_decode(codes)
+    q = _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+    N, K = q.shape
     if fmt == "fp8_b128":
         s = np.asarray(scales, dtype=np.float32).astype(np.float64)
-        return q * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+        return (q.reshape(N // 128, 128, K // 128, 128) * s[:, None, :, None]).reshape(N, K)
     if fmt == "mxfp8":
         s = e8m0_decode(scales)
-        return q * np.repeat(s, 32, axis=1)
+        return (q.reshape(N, K // 32, 32) * s[:, :, None]).reshape(N, K)
     raise ValueError(fmt)
+
+
+_E4M3_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
 
 
 # ------------------------------------------------- activation quantisation
@@ -238,6 +242,23 @@ def expert_ffn(X, wg, wu, wd, afmt):
     return hq @ wd.T
 
 
+def combine(y_perm, inv_pos, w, shared=None):
+    """Stage R's sum: out[t] = sum_j w[t,j] * y_perm[inv_pos[t*K+j]] (+ shared[t]);
+    slots with inv_pos < 0 contribute nothing."""
+    w = np.asarray(w, dtype=np.float64)
+    T, K = w.shape
+    inv = np.asarray(inv_pos).reshape(T, K)
+    y = np.asarray(y_perm, dtype=np.float64)
+    out = np.zeros((T, y.shape[1]))
+    for t in range(T):
+        for j in range(K):
+            if inv[t, j] >= 0:
+                out[t] += w[t, j] * y[inv[t, j]]
+    if shared is not None:
+        out += np.asarray(shared, dtype=np.float64)
+    return out
+
+
 class _Dequant:
     """Per-expert dequantisation with a small cache."""
 
@@ -290,11 +311,7 @@ def forward(cfg, x, w_router, bias, routed, shared):
     if shared is not None:
         wg, wu, wd = _Dequant(shared, shared.fmt)(0)
         S = expert_ffn(xf, wg, wu, wd, cfg.shared_afmt)
-    out = np.zeros((T, cfg.hidden))
-    for j in range(K):
-        out += r["w"][:, j:j + 1] * y_perm[inv_pos.reshape(T, K)[:, j]]
-    if S is not None:
-        out += S
+    out = combine(y_perm, inv_pos, r["w"], S)
     return OracleResult(r["logits"], r["ids"], r["w"], offsets, perm_src, inv_pos, y_perm, S, out)
 
 

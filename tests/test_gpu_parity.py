@@ -1,0 +1,308 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on MI355X.
+
+Bars: expert ids, dispatch offsets / permutation / inverse and quantised codes
+of x bit-exact; routing weights within 1e-4 relative (fp32 logits carry
+~1e-5 absolute error, and w moves with exp of it); layer output within
+max|err| / max|ref| <= 2e-2 of the unrounded fp64 oracle.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_router_amd as moe
+import oracle
+import synth
+from helpers import ensure_margin, rel_err, small_cfg
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+WTOL = 1e-4
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = {
+    "tiny_8tok": small_cfg(0),
+    "gemv_dsv2_3tok": small_cfg(1, tokens=3, hidden=384, n_experts=16, n_groups=4, topk_groups=2, topk=3,
+                                inter=256, shared_inter=256),
+    "b128_4exp_150tok": small_cfg(2, tokens=150, hidden=384, n_experts=4, n_groups=2, topk_groups=1, topk=2,
+                                  inter=256, shared_inter=384),
+    "b128_12exp_97tok": small_cfg(2, tokens=97, hidden=512, n_experts=12, n_groups=3, topk_groups=2, topk=3,
+                                  inter=384, shared_inter=256),
+    "mx_4exp_160tok": small_cfg(3, tokens=160, hidden=512, n_experts=4, inter=256, shared_inter=256),
+    "zipf_16exp_200tok": small_cfg(4, tokens=200, hidden=256, n_experts=16, n_groups=4, topk_groups=2, topk=4,
+                                   inter=128, shared_inter=128),
+    "flat_k1_64tok": small_cfg(0, tokens=64, n_experts=8, n_groups=1, topk_groups=1, topk=1, shared_inter=0),
+    "one_group_32tok": small_cfg(2, tokens=32, hidden=256, n_experts=16, n_groups=4, topk_groups=1, topk=2,
+                                 inter=128, shared_inter=128),
+}
+
+
+def gpu_inputs(cfg, with_experts=True):
+    say(f"[inputs] {cfg.name} T={cfg.tokens} H={cfg.hidden} E={cfg.n_experts}")
+    return ensure_margin(synth.make_inputs(cfg, DEV, with_experts=with_experts))
+
+
+def pairs_ok(cfg):
+    ok = {("bf16", "none"), ("fp8_b128", "fp8_1x128"), ("mxfp8", "mxfp8_1x32")}
+    return (cfg.routed_wfmt, cfg.routed_afmt) in ok and (cfg.shared_inter == 0 or
+                                                         (cfg.shared_wfmt, cfg.shared_afmt) in ok)
+
+
+# ---------------------------------------------------------------- codec
+
+def test_device_e4m3_codec_matches_oracle():
+    codes = torch.arange(256, dtype=torch.uint8, device=DEV)
+    out = torch.empty(256, dtype=torch.float32, device=DEV)
+    moe.e4m3_decode(codes, out)
+    torch.cuda.synchronize()
+    ref = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    got = out.cpu().double().numpy()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    rng = np.random.default_rng(11)
+    pos = np.arange(0, 0x7E, dtype=np.uint8)
+    mids = (oracle.e4m3_decode(pos) + oracle.e4m3_decode(pos + 1)) / 2
+    vals = np.concatenate([rng.standard_normal(50000) * s for s in (1e-3, 0.1, 1, 50, 400)] +
+                          [mids, -mids, [448.0, 460.0, 1e6, -1e6, 0.0, -0.0, 2.0 ** -10, 2.0 ** -11]]).astype(np.float32)
+    vt = torch.from_numpy(vals).to(DEV)
+    qc = torch.empty(vals.size, dtype=torch.uint8, device=DEV)
+    moe.e4m3_encode(vt, qc)
+    torch.cuda.synchronize()
+    want = oracle.e4m3_encode(vals.astype(np.float64))
+    got = qc.cpu().numpy()
+    # -0.0 and +0.0 both encode to a zero code; compare values for zeros
+    nz = vals != 0
+    assert np.array_equal(got[nz], want[nz])
+    assert np.all((got[~nz] & 0x7F) == 0)
+
+
+# ---------------------------------------------------------------- routing
+
+def _route(cfg, inp):
+    c = moe.make_config(cfg)
+    ws = moe.alloc_workspace(c, cfg.tokens)
+    ids = torch.empty(cfg.tokens, cfg.topk, dtype=torch.int32, device=DEV)
+    w = torch.empty(cfg.tokens, cfg.topk, dtype=torch.float32, device=DEV)
+    moe.route(c, inp.x, inp.w_router, inp.bias, ids, w, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _oracle_route(cfg, inp):
+    b = None if inp.bias is None else inp.bias.double().cpu().numpy()
+    return oracle.route(oracle.bf16_to_f64(inp.x), oracle.bf16_to_f64(inp.w_router), b, cfg)
+
+
+@pytest.mark.parametrize("name", list(SMALL) + ["full:" + c.name for c in synth.CONFIGS])
+def test_route(name):
+    cfg = SMALL[name] if name in SMALL else synth.get_config(name[5:])
+    inp = gpu_inputs(cfg, with_experts=False)
+    say(f"[route] {name}")
+    ids, w = _route(cfg, inp)
+    r = _oracle_route(cfg, inp)
+    assert np.array_equal(ids, r["ids"])
+    assert np.max(np.abs(w - r["w"]) / np.abs(r["w"])) <= WTOL
+
+
+# ---------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("afmt", ["none", "fp8_1x128", "mxfp8_1x32"])
+@pytest.mark.parametrize("T,E,K", [(1, 160, 6), (500, 160, 6), (333, 7, 3), (64, 256, 8)])
+def test_permute(T, E, K, afmt):
+    rng = np.random.default_rng(T * 7 + E + K)
+    if E == 160 and T > 1:   # skewed popularity, leaves some experts empty
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        ids = np.stack([rng.choice(E, K, replace=False, p=p / p.sum()) for _ in range(T)])
+    else:
+        ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    ids = ids.astype(np.int32)
+    cfg = small_cfg(2, tokens=T, hidden=256, n_experts=E, n_groups=1, topk_groups=1, topk=K, inter=128,
+                    shared_inter=0, routed_afmt=afmt, routed_wfmt={"none": "bf16", "fp8_1x128": "fp8_b128",
+                                                                   "mxfp8_1x32": "mxfp8"}[afmt])
+    say(f"[permute] T={T} E={E} K={K} {afmt}")
+    c = moe.make_config(cfg)
+    ws = moe.alloc_workspace(c, T)
+    x = synth.draw_tokens(cfg, DEV)
+    idt = torch.from_numpy(ids).to(DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    inv = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    if afmt == "none":
+        xp = torch.empty(T * K, 256, dtype=torch.bfloat16, device=DEV)
+        xs = None
+    else:
+        xp = torch.empty(T * K, 256, dtype=torch.uint8, device=DEV)
+        xs = torch.empty(T * K, 2 if afmt == "fp8_1x128" else 8, dtype=torch.float32 if afmt == "fp8_1x128" else torch.uint8,
+                         device=DEV)
+    moe.permute(c, idt, T, x, off, perm, inv, xp, xs, ws)
+    torch.cuda.synchronize()
+    o_off, o_perm, o_inv = oracle.permute(ids, E)
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    assert np.array_equal(perm.cpu().numpy(), o_perm)
+    assert np.array_equal(inv.cpu().numpy(), o_inv)
+    rows = oracle.bf16_to_f64(x)[o_perm // K]
+    if afmt == "none":
+        assert np.array_equal(oracle.bf16_to_f64(xp), rows)
+    else:
+        _, q, s = oracle.quant_act(rows, afmt, return_codes=True)
+        assert np.array_equal(xp.cpu().numpy(), q)
+        assert np.array_equal(xs.cpu().numpy(), s)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("name", ["tiny_8tok", "b128_4exp_150tok", "mx_4exp_160tok", "gemv_dsv2_3tok"])
+def test_expert_ffn(name, path, monkeypatch):
+    cfg = SMALL[name]
+    if path == "gemm" and not pairs_ok(cfg):
+        pytest.skip("no GEMM kernel for this format pair")
+    monkeypatch.setenv("MOE_FORCE_PATH", path)
+    inp = gpu_inputs(cfg)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    c = moe.make_config(cfg)
+    ws = moe.alloc_workspace(c, T)
+    xperm = inp.x[torch.from_numpy(r.perm_src // K).long().to(DEV)].contiguous()
+    off = torch.from_numpy(r.offsets).to(DEV)
+    y = torch.empty(T * K, H, dtype=torch.float32, device=DEV)
+    say(f"[expert_ffn routed] {name} {path}")
+    moe.expert_ffn(c, 0, xperm, None, T * K, off, moe.weights_of(inp.routed), y, ws)
+    torch.cuda.synchronize()
+    assert rel_err(y.cpu().numpy(), r.y_perm) <= TOL
+    if cfg.shared_inter:
+        ys = torch.empty(T, H, dtype=torch.float32, device=DEV)
+        say(f"[expert_ffn shared] {name} {path}")
+        moe.expert_ffn(c, 1, inp.x, None, T, None, moe.weights_of(inp.shared), ys, ws)
+        torch.cuda.synchronize()
+        assert rel_err(ys.cpu().numpy(), r.shared) <= TOL
+
+
+def test_expert_ffn_prequantised_rows(monkeypatch):
+    cfg = SMALL["b128_4exp_150tok"]
+    inp = gpu_inputs(cfg)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    c = moe.make_config(cfg)
+    ws = moe.alloc_workspace(c, T)
+    _, q, s = oracle.quant_act(oracle.bf16_to_f64(inp.x)[r.perm_src // K], "fp8_1x128", return_codes=True)
+    qt, st = torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
+    off = torch.from_numpy(r.offsets).to(DEV)
+    for path in ("gemv", "gemm"):
+        monkeypatch.setenv("MOE_FORCE_PATH", path)
+        y = torch.empty(T * K, H, dtype=torch.float32, device=DEV)
+        say(f"[expert_ffn prequantised] {path}")
+        moe.expert_ffn(c, 0, qt, st, T * K, off, moe.weights_of(inp.routed), y, ws)
+        torch.cuda.synchronize()
+        assert rel_err(y.cpu().numpy(), r.y_perm) <= TOL
+
+
+# ---------------------------------------------------------------- combine
+
+def test_combine():
+    rng = np.random.default_rng(5)
+    T, K, H, E = 37, 3, 384, 9
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    _, perm, inv = oracle.permute(ids, E)
+    yp = rng.standard_normal((T * K, H)).astype(np.float32)
+    ys = rng.standard_normal((T, H)).astype(np.float32)
+    w = rng.random((T, K)).astype(np.float32)
+    cfg = small_cfg(0, tokens=T, hidden=H, n_experts=E, n_groups=1, topk_groups=1, topk=K)
+    c = moe.make_config(cfg)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    for shared in (ys, None):
+        moe.combine(c, t(yp), t(inv), t(w), None if shared is None else t(shared), T, out)
+        torch.cuda.synchronize()
+        ref = oracle.combine(yp, inv, w, shared)
+        assert rel_err(oracle.bf16_to_f64(out), ref) <= 2.0 ** -8
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _forward(cfg, inp, x=None):
+    layer = moe.Layer(cfg, inp)
+    out, ids, w = layer.forward(x)
+    torch.cuda.synchronize()
+    return out, ids, w
+
+
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name, path, monkeypatch):
+    cfg = SMALL[name]
+    if path == "gemm" and not pairs_ok(cfg):
+        pytest.skip("no GEMM kernel for this format pair")
+    if path != "auto":
+        monkeypatch.setenv("MOE_FORCE_PATH", path)
+    inp = gpu_inputs(cfg)
+    say(f"[forward] {name} {path}")
+    out, ids, w = _forward(cfg, inp)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    assert np.array_equal(ids.cpu().numpy(), r.ids)
+    assert np.max(np.abs(w.cpu().numpy() - r.w) / r.w) <= WTOL
+    assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
+
+
+@pytest.mark.parametrize("cfgname", [c.name for c in synth.CONFIGS])
+def test_forward_full_size_sampled(cfgname):
+    """Full workload sizes, default path selection (the configuration the
+    benchmark times): every token's ids exact, sampled tokens' outputs."""
+    cfg = synth.get_config(cfgname)
+    inp = gpu_inputs(cfg)
+    say(f"[forward full] {cfgname}")
+    out, ids, w = _forward(cfg, inp)
+    r = _oracle_route(cfg, inp)
+    assert np.array_equal(ids.cpu().numpy(), r["ids"])
+    T = cfg.tokens
+    tokens = sorted(set([0, T - 1] + list(np.random.default_rng(3).choice(T, min(T, 6), replace=False))))
+    say(f"[oracle tokens] {tokens}")
+    _, _, ref = oracle.forward_tokens(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared, tokens)
+    got = oracle.bf16_to_f64(out[torch.tensor(tokens, device=DEV)])
+    assert rel_err(got, ref) <= TOL
+
+
+def test_forward_is_bitwise_deterministic():
+    cfg = SMALL["zipf_16exp_200tok"]
+    inp = gpu_inputs(cfg)
+    layer = moe.Layer(cfg, inp)
+    outs = []
+    for _ in range(3):
+        out, ids, w = layer.forward()
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy().copy(), ids.cpu().numpy().copy(), w.cpu().numpy().copy()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
+def test_forward_zero_tokens_is_noop():
+    cfg = SMALL["tiny_8tok"]
+    inp = synth.make_inputs(cfg, DEV)
+    layer = moe.Layer(cfg, inp)
+    out = torch.full((0, cfg.hidden), 7, dtype=torch.bfloat16, device=DEV)
+    layer.forward(inp.x[:0], out=out, ids=torch.empty(0, cfg.topk, dtype=torch.int32, device=DEV),
+                  w=torch.empty(0, cfg.topk, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+
+
+def test_forward_reuses_workspace_across_sizes():
+    """One workspace, calls with decreasing T (the route counter is left at 0)."""
+    cfg = SMALL["b128_12exp_97tok"]
+    inp = gpu_inputs(cfg)
+    layer = moe.Layer(cfg, inp)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    for T in (97, 40, 3, 1, 2, 97):
+        out, ids, _ = layer.forward(inp.x[:T].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), r.ids[:T])
+        # the per-token output does not depend on the other tokens
+        assert rel_err(oracle.bf16_to_f64(out), r.out[:T]) <= TOL
