@@ -10,7 +10,7 @@
 //             result is promoted into the accumulator with the block's
 //             activation scale (per row) times weight scale (per 128 rows)
 //   MXFP8     v_mfma_scale_f32_16x16x128_f8f6f4 with the e8m0 scales of A and
-//             B passed per lane: each lane's 32 K-values are one MX block
+//             B passed per lane (lane l scales row l%16, K block l/16)
 //
 // Tile: 64 rows x 256 columns x 128 bytes of K per step, 4 waves each owning
 // 16 rows x 256 columns.  Tiles of one step are staged in LDS with an XOR
@@ -179,11 +179,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         }
       }
     } else {
-      const int c0 = 2 * (lane >> 4);
+      // operand layout of the 16x16x128 8-bit instruction: lane group g = lane/16
+      // holds K [16g, 16g+16) in bytes 0-15 and K [64+16g, 64+16g+16) in bytes
+      // 16-31; the e8m0 scale of lane l covers row l%16, K block [32(l/16), +32)
+      const int c0 = lane >> 4;
       i32x8 a;
       {
         const i32x4 lo = *reinterpret_cast<const i32x4*>(&sA[buf][swz(arow_mfma, c0)]);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(&sA[buf][swz(arow_mfma, c0 + 1)]);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(&sA[buf][swz(arow_mfma, c0 + 4)]);
         a = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
       if (WF == W_FP8_B128) {
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         for (int j = 0; j < 16; ++j) {
           const int br = j * 16 + (lane & 15);
           const i32x4 lo = *reinterpret_cast<const i32x4*>(&sB[buf][swz(br, c0)]);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[buf][swz(br, c0 + 1)]);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[buf][swz(br, c0 + 4)]);
           const i32x8 b = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                             0, 127, 0, 127);
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         for (int j = 0; j < 16; ++j) {
           const int br = j * 16 + (lane & 15);
           const i32x4 lo = *reinterpret_cast<const i32x4*>(&sB[buf][swz(br, c0)]);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[buf][swz(br, c0 + 1)]);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[buf][swz(br, c0 + 4)]);
           const i32x8 b = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           const int sb = int((bsu[j][s] >> (8 * (lane >> 4))) & 0xffu);
           acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j], 0, 0, 0, sa, 0, sb);
