@@ -1,0 +1,234 @@
+"""Benchmark of one MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: the DeepSeek-V2 MoE layer at B=1 (hidden 5120, 160 routed
+experts in 8 groups of 20, top-3 groups, top-6 experts, route scale 16,
+intermediate 1536, shared experts fused to 3072, FP8 e4m3 weights with fp32
+per-128x128 block scales).  One step is one full layer forward (router,
+top-k, routed + shared FFNs, combine) on one token.  Steps cycle through 24
+replicas of the layer's inputs and weights (about 4.5 GB touched per cycle),
+so the 256 MB Infinity Cache cannot hold the working set and the weights
+stream from HBM, as they would across the layers of a model.
+
+Secondary: the 2,048-token layer (hidden 7168, 32 experts, top-4 flat
+routing, intermediate 2048, MXFP8 routed experts, bf16 shared expert), as
+effective TFLOP/s.
+
+Prints one JSON line.  Inputs are resident in HBM before the timed region.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer µs @B=1 (HBM GB/s, %peak); TFLOP/s @2048 tok (%FP8 MFMA peak)"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=24)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 2048-token workload")
+    ap.add_argument("--secondary-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def wbytes(ew, experts):
+    """Bytes of weights + scales of the listed experts of an ExpertWeights set."""
+    tot = 0
+    for t in (ew.gate, ew.up, ew.down, ew.gate_s, ew.up_s, ew.down_s):
+        if t is not None:
+            tot += t[0].numel() * t.element_size() * len(experts)
+    return tot
+
+
+def gate_up_bytes(ew, experts):
+    tot = 0
+    for t in (ew.gate, ew.up, ew.gate_s, ew.up_s):
+        if t is not None:
+            tot += t[0].numel() * t.element_size() * len(experts)
+    return tot
+
+
+class HostExperts:
+    """Host copies of a few experts, shaped like the generator's weight sets."""
+
+    def __init__(self, ew, experts):
+        self.fmt = ew.fmt
+        self.data = {int(e): ew.expert(int(e)) for e in experts}
+
+    def expert(self, e):
+        return self.data[int(e)]
+
+
+def time_layers(layers, xs, steps, warmup, torch):
+    n = len(layers)
+    for i in range(warmup):
+        layers[i % n].forward(xs[i % n])
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        layers[i % n].forward(xs[i % n])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall / steps * 1e3
+
+
+def trace_kernels(layers, xs, steps, moe, torch):
+    n = len(layers)
+    per = {}
+    with moe.LaunchTrace(64 * steps) as tr:
+        for i in range(steps):
+            layers[i % n].forward(xs[i % n])
+    for name, ms in tr.kernels():
+        per.setdefault(name, []).append(ms)
+    return {k: (statistics.mean(v), len(v) // steps) for k, v in per.items()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_router_amd as moe
+    import synth
+
+    dev = "cuda:0"
+    cfg = synth.get_config("dsv2_b1")
+    reps = [synth.make_inputs(cfg, dev, replica=r) for r in range(args.replicas)]
+    layers = [moe.Layer(cfg, inp) for inp in reps]
+    xs = [inp.x for inp in reps]
+    torch.cuda.synchronize()
+
+    ms_step, wall_ms = time_layers(layers, xs, args.steps, args.warmup, torch)
+    us = ms_step * 1e3
+
+    # algorithmic bytes per step, from each replica's actual routing
+    step_bytes, gu_bytes = [], []
+    for lay, inp in zip(layers, reps):
+        _, ids, _ = lay.forward()
+        torch.cuda.synchronize()
+        touched = sorted(set(ids.flatten().tolist()))
+        io = inp.x.numel() * 2 * 2
+        router = inp.w_router.numel() * 2
+        step_bytes.append(wbytes(inp.routed, touched) + wbytes(inp.shared, [0]) + router + io)
+        gu_bytes.append(gate_up_bytes(inp.routed, touched) + inp.x.numel() * 2)  # routed gate/up launch
+    bytes_step = statistics.mean(step_bytes)
+    gbps = bytes_step / (us * 1e-6) / 1e9
+
+    kern = trace_kernels(layers, xs, min(args.steps, 100), moe, torch)
+    dom = "gemv_gate_up"  # routed gate/up: the largest single stream (94 MB)
+    dom_us = kern[dom][0] * 1e3
+    dom_gbps = statistics.mean(gu_bytes) / (dom_us * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-weights/bf16-x/fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "DeepSeek-V2 MoE layer, B=1 decode: H=5120, 160 experts (8 groups x 20, top-3 groups, top-6), "
+                        "route scale 16, I=1536, fused shared 3072, FP8 e4m3 + fp32 128x128 block scales",
+            "tokens": 1,
+            "replicas": args.replicas,
+        },
+        "tokens_per_s": round(1e6 / us, 1),
+        "hbm_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": int(bytes_step),
+        "wall_ms_per_step": round(wall_ms, 6),
+        "kernels_us": {k: round(v[0] * 1e3, 3) for k, v in kern.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(dom_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(statistics.mean(gu_bytes)),
+            "launch_us": round(dom_us, 3),
+        },
+    }
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(args, moe, synth, torch)
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, reps[0], layers[0], torch)
+
+    print(json.dumps(out), flush=True)
+
+
+def secondary(args, moe, synth, torch):
+    cfg = synth.get_config("h7168_2048tok_mx")
+    inp = synth.make_inputs(cfg, "cuda:0")
+    lay = moe.Layer(cfg, inp)
+    ms, _ = time_layers([lay], [inp.x], args.secondary_steps, 3, torch)
+    T, H, K, I, Is, E = cfg.tokens, cfg.hidden, cfg.topk, cfg.inter, cfg.shared_inter, cfg.n_experts
+    flops = 2.0 * T * K * 3 * H * I + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
+    tflops = flops / (ms * 1e-3) / 1e12
+    kern = trace_kernels([lay], [inp.x], 5, moe, torch)
+    del lay, inp
+    torch.cuda.empty_cache()
+    return {
+        "workload": "2,048 tokens, H=7168, 32 experts flat top-4, I=2048, MXFP8 routed (e8m0 1x32) + bf16 shared 2048",
+        "us_per_layer": round(ms * 1e3, 2),
+        "tflops": round(tflops, 1),
+        "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "flops_per_layer": flops,
+        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in kern.items()},
+    }
+
+
+def cpu_baseline(cfg, inp, lay, torch):
+    """The fp64 oracle on the host cores, on the same B=1 layer (replica 0)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    _, ids, _ = lay.forward()
+    torch.cuda.synchronize()
+    touched = sorted(set(ids.flatten().tolist()))
+    routed = HostExperts(inp.routed, touched)
+    shared = HostExperts(inp.shared, [0])
+    x, wr = inp.x.cpu(), inp.w_router.cpu()
+    times = []
+    with threadpool_limits(limits=1):
+        deadline = time.perf_counter() + 20.0
+        while len(times) < 3 and (not times or time.perf_counter() < deadline):
+            t0 = time.perf_counter()
+            oracle.forward(cfg, x, wr, None, routed, shared)
+            times.append(time.perf_counter() - t0)
+    s = statistics.median(times)
+    return {"value": round(s * 1e6, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"the B=1 layer forward (replica 0), median of {len(times)} runs, "
+                      "float64 numpy with BLAS limited to one thread"}
+
+
+if __name__ == "__main__":
+    main()

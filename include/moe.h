@@ -193,6 +193,17 @@ moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_
 moe_status moe_debug_e4m3_decode(const uint8_t* codes, float* out, int32_t n, hipStream_t stream);
 moe_status moe_debug_e4m3_encode(const float* in, uint8_t* codes, int32_t n, hipStream_t stream);
 
+/* Measurement hook: arm (events != NULL, n_events >= 2) or disarm (NULL) a
+ * launch trace.  While armed, each kernel launch of the entry points records
+ * events[2i] before and events[2i+1] after launch i on the call's stream,
+ * for the first n_events/2 launches since arming.  The caller creates the
+ * events (with timing) and keeps them alive while armed.  Process-global and
+ * not thread-safe: one benchmarking thread at a time. */
+moe_status moe_debug_trace(hipEvent_t* events /*host array*/, int32_t n_events);
+/* Launches recorded since the trace was armed, and the kernel name of one. */
+int32_t moe_debug_trace_count(void);
+const char* moe_debug_trace_name(int32_t i);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,9 @@ def _lib():
                                    _vp, _sz, _vp]),
             "moe_debug_e4m3_decode": (_i32, [_vp, _vp, _i32, _vp]),
             "moe_debug_e4m3_encode": (_i32, [_vp, _vp, _i32, _vp]),
+            "moe_debug_trace": (_i32, [_vp, _i32]),
+            "moe_debug_trace_count": (_i32, []),
+            "moe_debug_trace_name": (ctypes.c_char_p, [_i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -72,7 +75,8 @@ def _lib():
 
 
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode")
+           "moe_combine", "moe_forward", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
+           "moe_debug_trace_count", "moe_debug_trace_name")
 
 
 def _ptr(t):
@@ -157,6 +161,38 @@ def e4m3_decode(codes, out, stream=None):
 
 def e4m3_encode(vals, codes, stream=None):
     _check(_lib().moe_debug_e4m3_encode(_ptr(vals), _ptr(codes), vals.numel(), _stream(stream)), "e4m3_encode")
+
+
+class LaunchTrace:
+    """Bracket every kernel launch of the library with HIP events (measurement only).
+
+    with LaunchTrace(max_launches) as tr:
+        ...calls...
+    tr.kernels() -> [(name, ms), ...] after a synchronize.
+    """
+
+    def __init__(self, max_launches=4096):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+
+    def __enter__(self):
+        for e in self.events:   # torch creates the HIP event on first record
+            e.record()
+        torch.cuda.synchronize()
+        handles = [e.cuda_event for e in self.events]
+        if not all(handles):
+            raise RuntimeError("torch did not create the HIP events")
+        self._arr = (ctypes.c_void_p * len(self.events))(*handles)
+        _check(_lib().moe_debug_trace(self._arr, len(self.events)), "moe_debug_trace")
+        return self
+
+    def __exit__(self, *exc):
+        self.n = _lib().moe_debug_trace_count()
+        self.names = [_lib().moe_debug_trace_name(i).decode() for i in range(self.n)]
+        _lib().moe_debug_trace(None, 0)
+
+    def kernels(self):
+        torch.cuda.synchronize()
+        return [(self.names[i], self.events[2 * i].elapsed_time(self.events[2 * i + 1])) for i in range(self.n)]
 
 
 class Layer:

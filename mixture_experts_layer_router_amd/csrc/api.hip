@@ -145,12 +145,34 @@ RouteParams route_params(const moe_config* c) {
     if ((expr) != hipSuccess) return MOE_EHIP;    \
   } while (0)
 
+// Optional launch trace for measurement: when armed, every kernel launch of
+// the entry points is bracketed by two caller-owned events recorded on the
+// launch stream.  Not thread-safe; meant for one benchmarking thread.
+struct Trace {
+  hipEvent_t* ev = nullptr;
+  int max = 0;
+  int n = 0;
+  const char* names[128] = {};
+} g_trace;
+
+template <class F>
+hipError_t traced(const char* name, hipStream_t s, F&& f) {
+  if (!g_trace.ev || 2 * g_trace.n + 1 >= g_trace.max || g_trace.n >= 128) return f();
+  if (hipEventRecord(g_trace.ev[2 * g_trace.n], s) != hipSuccess) return hipErrorUnknown;
+  const hipError_t e = f();
+  if (hipEventRecord(g_trace.ev[2 * g_trace.n + 1], s) != hipSuccess) return hipErrorUnknown;
+  g_trace.names[g_trace.n++] = name;
+  return e;
+}
+#define LAUNCH(name, expr) HIP_TRY(traced(name, s_, [&] { return (expr); }))
+
 moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_t* wr, const float* bias, int* ids,
                     float* w, void* ws, const Ws& L, hipStream_t s) {
   const RouteParams rp = route_params(c);
+  hipStream_t s_ = s;
   if (T <= kRouteGemvMaxT) {
-    HIP_TRY(launch_route_gemv_topk(x, T, wr, bias, rp, at<float>(ws, L.logits), at<unsigned>(ws, L.counter), ids, w,
-                                   s));
+    LAUNCH("route_logits", launch_route_logits(x, T, wr, rp, at<float>(ws, L.logits), s));
+    LAUNCH("topk", launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s));
     return MOE_OK;
   }
   GemmParams g{};
@@ -162,8 +184,8 @@ moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_
   g.M = T;
   g.C = at<float>(ws, L.logits);
   g.ldc = c->n_experts;
-  HIP_TRY(launch_gemm(W_BF16, EPI_F32, g, s));
-  HIP_TRY(launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s));
+  LAUNCH("gemm_router_logits", launch_gemm(W_BF16, EPI_F32, g, s));
+  LAUNCH("topk", launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s));
   return MOE_OK;
 }
 
@@ -177,6 +199,7 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   const int af = routed ? c->routed_afmt : c->shared_afmt;
   const int I = routed ? c->inter : c->shared_inter;
   const int H = c->hidden;
+  hipStream_t s_ = s;
   GemmParams g{};
   g.A = A;
   g.lda = H;
@@ -200,7 +223,7 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   g.ldc = I;
   g.Cs = hs;
   g.out_afmt = af;
-  HIP_TRY(launch_gemm(wf, EPI_GATEUP, g, s));
+  LAUNCH(routed ? "gemm_gate_up_routed" : "gemm_gate_up_shared", launch_gemm(wf, EPI_GATEUP, g, s));
   GemmParams d{};
   d.A = h;
   d.lda = I;
@@ -218,7 +241,7 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   d.max_tiles = maxt;
   d.C = y;
   d.ldc = H;
-  HIP_TRY(launch_gemm(wf, y_bf16 ? EPI_BF16 : EPI_F32, d, s));
+  LAUNCH(routed ? "gemm_down_routed" : "gemm_down_shared", launch_gemm(wf, y_bf16 ? EPI_BF16 : EPI_F32, d, s));
   return MOE_OK;
 }
 
@@ -263,6 +286,7 @@ moe_status moe_route(const moe_config* cfg, const uint16_t* x, int32_t T, const 
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T, const uint16_t* x,
                        int32_t* expert_offsets, int32_t* perm_src, int32_t* inv_pos, void* x_perm,
                        void* x_perm_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hipStream_t s_ = stream;
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
@@ -274,10 +298,10 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
   const Ws L = plan(cfg, T);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
   const int TK = T * cfg->topk;
-  HIP_TRY(launch_permute(topk_ids, TK, cfg->n_experts, expert_offsets, perm_src, inv_pos, nullptr, nullptr, kGemmBM,
+  LAUNCH("permute", launch_permute(topk_ids, TK, cfg->n_experts, expert_offsets, perm_src, inv_pos, nullptr, nullptr, kGemmBM,
                          stream));
   if (x_perm)
-    HIP_TRY(launch_quant_rows(x, false, TK, cfg->hidden, perm_src, cfg->topk, cfg->routed_afmt, x_perm, x_perm_scale,
+    LAUNCH("quant_rows", launch_quant_rows(x, false, TK, cfg->hidden, perm_src, cfg->topk, cfg->routed_afmt, x_perm, x_perm_scale,
                               nullptr, stream));
   return MOE_OK;
 }
@@ -285,6 +309,7 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, const void* x_scale, int32_t rows,
                           const int32_t* seg_offsets, const moe_ffn_weights* W, float* y, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
+  hipStream_t s_ = stream;
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (which != 0 && which != 1) return MOE_EINVAL;
@@ -311,11 +336,11 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
     const void* xin = x;
     bool xf32 = false;
     if (x_scale) {  // pre-quantised rows: dequantise to fp32
-      HIP_TRY(launch_dequant_rows(static_cast<const uint8_t*>(x), x_scale, af, rows, H, at<float>(ws, L.xq), stream));
+      LAUNCH("dequant_rows", launch_dequant_rows(static_cast<const uint8_t*>(x), x_scale, af, rows, H, at<float>(ws, L.xq), stream));
       xin = at<float>(ws, L.xq);
       xf32 = true;
     } else if (af != A_NONE) {
-      HIP_TRY(launch_quant_rows(x, false, rows, H, nullptr, 1, af, nullptr, nullptr, at<float>(ws, L.xq), stream));
+      LAUNCH("quant_rows", launch_quant_rows(x, false, rows, H, nullptr, 1, af, nullptr, nullptr, at<float>(ws, L.xq), stream));
       xin = at<float>(ws, L.xq);
       xf32 = true;
     }
@@ -343,8 +368,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
       u.I = 128;
       u.hs = h;
     }
-    HIP_TRY(launch_gemv_gate_up(u, stream));
-    if (af != A_NONE) HIP_TRY(launch_quant_rows(h, true, rows, I, nullptr, 1, af, nullptr, nullptr, h, stream));
+    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
+    if (af != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, rows, I, nullptr, 1, af, nullptr, nullptr, h, stream));
     GemvDownParams d{};
     d.wfmt = wf;
     d.swfmt = wf;
@@ -357,7 +382,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
     } else {
       d.Is = I; d.hs = h; d.sd = W->down; d.sds = W->down_s;
     }
-    HIP_TRY(launch_gemv_down(d, stream));
+    LAUNCH("gemv_down", launch_gemv_down(d, stream));
     return MOE_OK;
   }
 
@@ -365,7 +390,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
   const void* A = x;
   const void* As = x_scale;
   if (!x_scale && af != A_NONE) {
-    HIP_TRY(launch_quant_rows(x, false, rows, H, nullptr, 1, af, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
+    LAUNCH("quant_rows", launch_quant_rows(x, false, rows, H, nullptr, 1, af, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
                               stream));
     A = at<void>(ws, L.xq);
     As = at<void>(ws, L.xqs);
@@ -377,7 +402,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
     tiles = at<int>(ws, L.tiles);
     ntiles = at<int>(ws, L.ntiles);
     maxt = max_tiles(rows, E, kGemmBM);
-    HIP_TRY(launch_build_tiles(seg_offsets, E, rows, kGemmBM, tiles, ntiles, stream));
+    LAUNCH("build_tiles", launch_build_tiles(seg_offsets, E, rows, kGemmBM, tiles, ntiles, stream));
   }
   return gemm_ffn(cfg, routed, A, As, nullptr, 1, rows, routed ? seg_offsets : nullptr, tiles, ntiles, maxt, W,
                   at<void>(ws, routed ? L.h : L.hsh), at<void>(ws, routed ? L.hs : L.hshs), y, false, stream);
@@ -385,19 +410,21 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
 
 moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* inv_pos, const float* topk_w,
                        const float* y_shared, int32_t T, uint16_t* out, hipStream_t stream) {
+  hipStream_t s_ = stream;
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   if (!y_perm || !inv_pos || !topk_w || !out) return MOE_EINVAL;
   if (!aligned16(y_perm) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_EALIGN;
-  HIP_TRY(launch_combine(y_perm, false, inv_pos, topk_w, y_shared, false, T, cfg->topk, cfg->hidden, out, stream));
+  LAUNCH("combine", launch_combine(y_perm, false, inv_pos, topk_w, y_shared, false, T, cfg->topk, cfg->hidden, out, stream));
   return MOE_OK;
 }
 
 moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
                        const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared, uint16_t* out,
                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hipStream_t s_ = stream;
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
@@ -421,13 +448,92 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
   const bool gemv = fp == 1 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
 
-  if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
-
-  if (gemv) {
+  if (gemv && T <= kRouteGemvMaxT) {
+    // small T: router || shared gate/up, then top-k || shared down, then the
+    // routed experts; the kernel boundaries are the only synchronisation
+    const void* xs = x;
+    bool xs32 = false;
+    if (has_shared && saf != A_NONE) {
+      LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
+      xs = at<float>(ws, L.xs2);
+      xs32 = true;
+    }
+    DecodeParams dp{};
+    dp.x = x;
+    dp.T = T;
+    dp.H = H;
+    dp.wr = w_router;
+    dp.bias = bias;
+    dp.rp = route_params(cfg);
+    dp.logits = at<float>(ws, L.logits);
+    dp.ids = ids;
+    dp.w = w;
+    dp.swfmt = has_shared ? cfg->shared_wfmt : W_BF16;
+    if (has_shared) {
+      dp.xs = xs;
+      dp.xs_f32 = xs32;
+      dp.sg = shared->gate; dp.su = shared->up; dp.sgs = shared->gate_s; dp.sus = shared->up_s;
+      dp.sd = shared->down; dp.sds = shared->down_s;
+      dp.Is = cfg->shared_inter;
+      dp.hs = at<float>(ws, L.hsh);
+      dp.ysh = at<float>(ws, L.ysh);
+    }
+    LAUNCH("decode_router_shared_up", launch_decode_stage1(dp, stream));
+    if (has_shared && saf != A_NONE)
+      LAUNCH("quant_rows", launch_quant_rows(dp.hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, dp.hs, stream));
+    LAUNCH("decode_topk_shared_down", launch_decode_stage2(dp, stream));
     const void* xr = x;
     bool xr32 = false;
     if (raf != A_NONE) {
-      HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
+      if (saf == raf && has_shared) {
+        xr = xs;
+      } else {
+        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
+        xr = at<float>(ws, L.xq);
+      }
+      xr32 = true;
+    }
+    float* h = at<float>(ws, L.h);
+    GemvUpParams u{};
+    u.wfmt = cfg->routed_wfmt;
+    u.swfmt = cfg->routed_wfmt;
+    u.x = xr;
+    u.x_f32 = xr32;
+    u.T = T;
+    u.H = H;
+    u.ids = ids;
+    u.K = K;
+    u.g = routed->gate; u.u = routed->up; u.gs = routed->gate_s; u.us = routed->up_s;
+    u.I = cfg->inter;
+    u.h = h;
+    u.E = E;
+    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
+    if (raf != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
+    GemvDownParams d{};
+    d.wfmt = cfg->routed_wfmt;
+    d.swfmt = cfg->routed_wfmt;
+    d.T = T;
+    d.H = H;
+    d.K = K;
+    d.I = cfg->inter;
+    d.ids = ids;
+    d.w = w;
+    d.h = h;
+    d.d = routed->down; d.ds = routed->down_s;
+    d.out = out;
+    d.E = E;
+    d.ys_add = has_shared ? dp.ysh : nullptr;
+    LAUNCH("gemv_down_combine", launch_gemv_down(d, stream));
+    return MOE_OK;
+  }
+
+  if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
+
+  if (gemv) {  // T > kRouteGemvMaxT on the GEMV path: routed + shared gate/up in one launch
+    const void* xr = x;
+    bool xr32 = false;
+    if (raf != A_NONE) {
+      LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
       xr = at<float>(ws, L.xq);
       xr32 = true;
     }
@@ -437,7 +543,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
       if (saf == raf) {
         xs = xr;
       } else {
-        HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
+        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
         xs = at<float>(ws, L.xs2);
       }
       xs32 = true;
@@ -464,10 +570,10 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
       u.xs_f32 = xs32;
     }
     u.E = E;
-    HIP_TRY(launch_gemv_gate_up(u, stream));
-    if (raf != A_NONE) HIP_TRY(launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
+    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
+    if (raf != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
     if (has_shared && saf != A_NONE)
-      HIP_TRY(launch_quant_rows(hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, hs, stream));
+      LAUNCH("quant_rows", launch_quant_rows(hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, hs, stream));
     GemvDownParams d{};
     d.wfmt = cfg->routed_wfmt;
     d.swfmt = u.swfmt;
@@ -484,7 +590,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
     if (has_shared) { d.sd = shared->down; d.sds = shared->down_s; }
     d.out = out;
     d.E = E;
-    HIP_TRY(launch_gemv_down(d, stream));
+    LAUNCH("gemv_down_combine", launch_gemv_down(d, stream));
     return MOE_OK;
   }
 
@@ -494,11 +600,11 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   int* inv = at<int>(ws, L.inv);
   int* tiles = at<int>(ws, L.tiles);
   int* ntiles = at<int>(ws, L.ntiles);
-  HIP_TRY(launch_permute(ids, TK, E, off, perm, inv, tiles, ntiles, kGemmBM, stream));
+  LAUNCH("permute", launch_permute(ids, TK, E, off, perm, inv, tiles, ntiles, kGemmBM, stream));
   const void* xa = x;
   const void* xas = nullptr;
   if (raf != A_NONE) {
-    HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, raf, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
+    LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
                               stream));
     xa = at<void>(ws, L.xq);
     xas = at<void>(ws, L.xqs);
@@ -515,7 +621,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
         xs = xa;
         xss = xas;
       } else {
-        HIP_TRY(launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
+        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
                                   nullptr, stream));
         xs = at<void>(ws, L.xs2);
         xss = at<void>(ws, L.xs2s);
@@ -526,21 +632,37 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
                        at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
       return st;
   }
-  HIP_TRY(launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
+  LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
   return MOE_OK;
 }
 
+moe_status moe_debug_trace(hipEvent_t* events, int32_t n_events) {
+  if (events && n_events < 2) return MOE_EINVAL;
+  g_trace.ev = events;
+  g_trace.max = events ? n_events : 0;
+  g_trace.n = 0;
+  return MOE_OK;
+}
+
+int32_t moe_debug_trace_count(void) { return g_trace.n; }
+
+const char* moe_debug_trace_name(int32_t i) {
+  return (i >= 0 && i < g_trace.n && i < 128) ? g_trace.names[i] : "";
+}
+
 moe_status moe_debug_e4m3_decode(const uint8_t* codes, float* out, int32_t n, hipStream_t stream) {
+  hipStream_t s_ = stream;
   if (n < 0 || (n > 0 && (!codes || !out))) return MOE_EINVAL;
   if (n == 0) return MOE_OK;
-  HIP_TRY(launch_e4m3_decode(codes, out, n, stream));
+  LAUNCH("e4m3_decode", launch_e4m3_decode(codes, out, n, stream));
   return MOE_OK;
 }
 
 moe_status moe_debug_e4m3_encode(const float* in, uint8_t* codes, int32_t n, hipStream_t stream) {
+  hipStream_t s_ = stream;
   if (n < 0 || (n > 0 && (!codes || !in))) return MOE_EINVAL;
   if (n == 0) return MOE_OK;
-  HIP_TRY(launch_e4m3_encode(in, codes, n, stream));
+  LAUNCH("e4m3_encode", launch_e4m3_encode(in, codes, n, stream));
   return MOE_OK;
 }
 

@@ -10,6 +10,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -72,21 +73,55 @@ MOE_DEV int mx_exponent(float amax) {
 MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // ---------------------------------------------------------------- wave64 reductions
-MOE_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// DPP lane moves (GFX9 DPP controls): quad_perm [1,0,3,2] = 0xb1 (xor 1),
+// quad_perm [2,3,0,1] = 0x4e (xor 2), row_half_mirror = 0x141 (lane i <- 7-i
+// within 8), row_mirror = 0x140 (lane i <- 15-i within 16), row_bcast:15 =
+// 0x142 (row r+1 <- lane 15 of row r), row_bcast:31 = 0x143 (rows 2,3 <- lane 31).
+// Lanes of rows outside row_mask keep `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+MOE_DEV float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
+}
+
+// reduction within each row of 16 lanes; every lane of the row gets the result
+MOE_DEV float row16_sum(float v) {
+  v += dpp_f<0xb1>(0.f, v);
+  v += dpp_f<0x4e>(0.f, v);
+  v += dpp_f<0x141>(0.f, v);
+  v += dpp_f<0x140>(0.f, v);
   return v;
+}
+MOE_DEV float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v, v));
+  v = fmaxf(v, dpp_f<0x4e>(v, v));
+  v = fmaxf(v, dpp_f<0x141>(v, v));
+  v = fmaxf(v, dpp_f<0x140>(v, v));
+  return v;
+}
+// sum / max over the whole wave, returned uniform (read from lane 63)
+MOE_DEV float wave_sum(float v) {
+  v = row16_sum(v);
+  v += dpp_f<0x142, 0xa>(0.f, v);
+  v += dpp_f<0x143, 0xc>(0.f, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 MOE_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  v = fmaxf(v, dpp_f<0x142, 0xa>(v, v));
+  v = fmaxf(v, dpp_f<0x143, 0xc>(v, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
-// max over aligned groups of `w` lanes (w a power of two <= 64)
+// max over aligned groups of W lanes (W = 4 or 16); every lane of the group gets it
 template <int W>
 MOE_DEV float group_max(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  static_assert(W == 4 || W == 16, "group of 4 or 16 lanes");
+  v = fmaxf(v, dpp_f<0xb1>(v, v));
+  v = fmaxf(v, dpp_f<0x4e>(v, v));
+  if (W == 16) {
+    v = fmaxf(v, dpp_f<0x141>(v, v));
+    v = fmaxf(v, dpp_f<0x140>(v, v));
+  }
   return v;
 }
 

@@ -71,18 +71,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const size_t lda_b = size_t(p.lda) * esz<WF>();
   const size_t ldb_b = size_t(K) * esz<WF>();
 
-  auto phys_row = [&](int rl) -> int {
-    const int r = seg0 + m0 + min(rl, mrows - 1);
-    return p.a_map ? p.a_map[r] / p.a_div : r;
-  };
+#define PHYS_ROW(rl) (p.a_map ? p.a_map[seg0 + m0 + min((rl), mrows - 1)] / p.a_div : seg0 + m0 + min((rl), mrows - 1))
   const uint8_t* b0 = static_cast<const uint8_t*>(p.B0) + size_t(e) * p.b_stride * esz<WF>();
   const uint8_t* b1 = p.B1 ? static_cast<const uint8_t*>(p.B1) + size_t(e) * p.b_stride * esz<WF>() : nullptr;
-  auto brow_ptr = [&](int nl) -> const uint8_t* {
-    if (EPI == EPI_GATEUP) {
-      return nl < BN / 2 ? b0 + size_t(n0 + nl) * ldb_b : b1 + size_t(n0 + nl - BN / 2) * ldb_b;
-    }
-    return b0 + size_t(min(n0 + nl, p.N - 1)) * ldb_b;
-  };
 
   // this thread's global->LDS chunks: A 2, B 8
   const uint8_t* ga[2];
@@ -90,7 +81,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    ga[i] = static_cast<const uint8_t*>(p.A) + size_t(phys_row(r)) * lda_b + c * 16;
+    ga[i] = static_cast<const uint8_t*>(p.A) + size_t(PHYS_ROW(r)) * lda_b + c * 16;
     la[i] = swz(r, c);
   }
   const uint8_t* gb[8];
@@ -98,7 +89,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    gb[i] = brow_ptr(r) + c * 16;
+    const uint8_t* rp;
+    if (EPI == EPI_GATEUP)
+      rp = r < BN / 2 ? b0 + size_t(n0 + r) * ldb_b : b1 + size_t(n0 + r - BN / 2) * ldb_b;
+    else
+      rp = b0 + size_t(min(n0 + r, p.N - 1)) * ldb_b;
+    gb[i] = rp + c * 16;
     lb[i] = swz(r, c);
   }
 
@@ -106,11 +102,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const int arow_mfma = wave * 16 + (lane & 15);  // A row of this lane in the MFMA operand layout
   int srow[4];                                     // A rows of this lane's accumulator elements
 #pragma unroll
-  for (int i = 0; i < 4; ++i) srow[i] = phys_row(wave * 16 + 4 * (lane >> 4) + i);
+  for (int i = 0; i < 4; ++i) srow[i] = PHYS_ROW(wave * 16 + 4 * (lane >> 4) + i);
   const int kb_per_row = K / 128;
   const float* asf = static_cast<const float*>(p.As);
   const uint32_t* asu = static_cast<const uint32_t*>(p.As);
-  const int amx_row = phys_row(arow_mfma);
+  const int amx_row = PHYS_ROW(arow_mfma);
+#undef PHYS_ROW
   const float* bsf0 = nullptr;
   const float* bsf1 = nullptr;
   const uint32_t* bsu[16];
@@ -146,27 +143,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[2], rb[8];
-  auto gload = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const uint4*>(ga[i] + size_t(s) * BKB);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const uint4*>(gb[i] + size_t(s) * BKB);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&sA[buf][la[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&sB[buf][lb[i]]) = rb[i];
-  };
+  u32x4 ra[2], rb[8];
+#define GLOAD(st)                                                                          \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) ra[i] =                                  \
+        *reinterpret_cast<const u32x4*>(ga[i] + size_t(st) * BKB);                         \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) rb[i] =                                  \
+        *reinterpret_cast<const u32x4*>(gb[i] + size_t(st) * BKB);                         \
+  } while (0)
+#define LSTORE(bf)                                                                          \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&sA[bf][la[i]]) = ra[i]; \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sB[bf][lb[i]]) = rb[i]; \
+  } while (0)
 
-  gload(0);
-  lstore(0);
+  GLOAD(0);
+  LSTORE(0);
   __syncthreads();
 
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nk) gload(s + 1);
+    if (s + 1 < nk) GLOAD(s + 1);
     if (WF == W_BF16) {
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
@@ -219,10 +216,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         }
       }
     }
-    if (s + 1 < nk) lstore(buf ^ 1);
+    if (s + 1 < nk) LSTORE(buf ^ 1);
     __syncthreads();
   }
 
+#undef GLOAD
+#undef LSTORE
   // ------------------------------------------------------------ epilogue
   const int col_l = lane & 15;
 #pragma unroll

@@ -1,52 +1,90 @@
 // Small-batch expert FFN as bandwidth-bound GEMVs ("From 35 to 873
 // tokens/s", Skill 5: decode is a GEMV; the BS=1 GEMM is bandwidth bound).
 //
-// gate/up: one wave per (slot, block of 8 intermediate rows) reads 8 gate and
-// 8 up weight rows once with 16-byte lane loads (1 KB per wave per row chunk,
-// fully coalesced), converts FP8 codes with the hardware e4m3 converter,
-// accumulates in fp32 against the token's row, applies the per-block scale
-// once per 16-element lane chunk, and writes h = SiLU(g) * u (stages P1/Q1).
+// gate/up (stages P1/Q1): one wave per (slot, block of 4 intermediate
+// columns) streams the 4 gate and 4 up weight rows with 16-byte lane loads
+// (1 KB contiguous per wave per row and chunk); each chunk's 8 loads are
+// issued together and many resident waves keep HBM busy.
+// FP8 codes go through the hardware e4m3 converter, the products accumulate
+// in fp32 against the token's row, the block scale is applied once per
+// 16-element lane chunk, and the wave writes h = SiLU(g) * u.
 //
-// down: one wave per (token, block of 8 output rows) walks the concatenation
-// of the token's K routed down matrices and the shared one (stages P2/Q2),
-// folding each routing weight into the block scale, and writes the bf16
-// output directly: the combine of stage R happens in registers, in a fixed
-// order, with one rounding.
+// down (stages P2/Q2 and the sum of R): one workgroup per (token, block of 8
+// output rows).  Its K dimension is the concatenation of the token's K routed
+// down matrices and the shared one; the 4 waves take chunks of it round robin,
+// fold each routing weight into the block scale, and their partial sums are
+// added through LDS in wave order.  The bf16 output is written directly: the
+// combine happens in registers, in a fixed order, with one rounding.
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int RB = 8;  // rows per wave item
+constexpr int RU = 4;  // intermediate columns per gate/up wave item (4 gate + 4 up rows)
+constexpr int CPI = 2; // weight chunks whose loads are issued together in the gate/up loop
+constexpr int RD = 8;  // output rows per down workgroup
+constexpr int DW = 4;  // waves per down workgroup
 
-// elements per 16-byte lane load
 template <int WF>
-struct Epl {
-  static constexpr int v = (WF == W_BF16) ? 8 : 16;
+struct Fmt {
+  static constexpr int EPL = (WF == W_BF16) ? 8 : 16;  // elements per 16-byte lane load
+  static constexpr int CW = 64 * EPL;                  // elements per wave chunk
+  static constexpr int ES = (WF == W_BF16) ? 2 : 1;    // bytes per element
 };
 
 // partial dot of one 16-byte weight chunk with EPL x values
 template <int WF>
-MOE_DEV float dot_chunk(uint4 w, const float* x) {
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+MOE_DEV float dot_chunk(u32x4 w, const float* x) {
   float s0 = 0.f, s1 = 0.f;
   if (WF == W_BF16) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      s0 = fmaf(__uint_as_float(u[q] << 16), x[2 * q], s0);
-      s1 = fmaf(__uint_as_float(u[q] & 0xffff0000u), x[2 * q + 1], s1);
+      s0 = fmaf(__uint_as_float(w[q] << 16), x[2 * q], s0);
+      s1 = fmaf(__uint_as_float(w[q] & 0xffff0000u), x[2 * q + 1], s1);
     }
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f32x2 a = e4m3x2_to_f32(u[q], false);
-      f32x2 b = e4m3x2_to_f32(u[q], true);
+      const f32x2 a = e4m3x2_to_f32(w[q], false);
+      const f32x2 b = e4m3x2_to_f32(w[q], true);
       s0 = fmaf(a.x, x[4 * q + 0], s0);
       s1 = fmaf(a.y, x[4 * q + 1], s1);
       s0 = fmaf(b.x, x[4 * q + 2], s0);
       s1 = fmaf(b.y, x[4 * q + 3], s1);
+    }
+  }
+  return s0 + s1;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// partial dot of one 16-byte weight chunk with EPL bf16 activations held as
+// packed pairs: FP8 codes go to bf16 pairs with the gfx950 scaled converter
+// (exact: every e4m3 value is a bf16 value) and v_dot2_f32_bf16 accumulates
+// two products per instruction in fp32; bf16 weights feed v_dot2 directly.
+MOE_DEV bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+template <int WF>
+MOE_DEV float dot_chunk_bx(u32x4 w, const uint32_t* xp) {
+  // words are taken out of the vector before any bit_cast: bit-casting a
+  // vector element directly was lowered to the wrong register
+  const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
+  float s0 = 0.f, s1 = 0.f;
+  if (WF == W_BF16) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wq[0]), as_bf16x2(xp[0]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wq[1]), as_bf16x2(xp[1]), s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wq[2]), as_bf16x2(xp[2]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wq[3]), as_bf16x2(xp[3]), s1, false);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wq[q], 1.0f, false);
+      const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wq[q], 1.0f, true);
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(a, as_bf16x2(xp[2 * q]), s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(b, as_bf16x2(xp[2 * q + 1]), s1, false);
     }
   }
   return s0 + s1;
@@ -61,91 +99,143 @@ MOE_DEV float wscale(const void* S, int n, int k, int L) {
 }
 
 template <int WF>
-MOE_DEV constexpr int esize() { return WF == W_BF16 ? 2 : 1; }
+MOE_DEV size_t wstride(int N, int L) { return size_t(N) * L * Fmt<WF>::ES; }
+template <int WF>
+MOE_DEV size_t sstride(int N, int L) {
+  return WF == W_FP8_B128 ? size_t(N / 128) * (L / 128) * 4 : (WF == W_MXFP8 ? size_t(N) * (L / 32) : 0);
+}
 
-template <bool F32>
-MOE_DEV void load_x(const void* x, size_t off, float* v, int n) {
+// EPL activation values at x[off..off+EPL) as fp32 (x is fp32 or bf16)
+template <bool F32, int EPL>
+MOE_DEV void load_x(const void* x, size_t off, float (&v)[EPL]) {
   if (F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-    for (int i = 0; i < n / 4; ++i) {
-      float4 f = p[i];
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + off + 4 * i);
       v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
     }
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
-    for (int i = 0; i < n / 8; ++i) {
-      uint4 u = p[i];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < EPL / 8; ++i) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + off + 8 * i);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v[8 * i + 2 * q] = __uint_as_float(w[q] << 16);
-        v[8 * i + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        v[8 * i + 2 * q] = __uint_as_float(u[q] << 16);
+        v[8 * i + 2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
       }
     }
   }
 }
 
-// h[i0 .. i0+RB) = SiLU(x.Wg^T) * (x.Wu^T) for one x row.
-template <int WF, bool XF32>
+// One register stage of the gate/up stream: NR gate rows, NR up rows, x
+// (fp32, or packed bf16 pairs when the activations are bf16), scales.
+template <int WF, bool XF32, int NR = RU>
+struct UpStage {
+  u32x4 g[NR], u[NR];
+  float x[XF32 ? Fmt<WF>::EPL : 1];
+  uint32_t xp[XF32 ? 1 : Fmt<WF>::EPL / 2];
+  float sg[NR], su[NR];
+};
+
+template <int WF, bool XF32, int NR>
+MOE_DEV float up_dot(u32x4 w, const UpStage<WF, XF32, NR>& st) {
+  if constexpr (XF32) return dot_chunk<WF>(w, st.x);
+  else return dot_chunk_bx<WF>(w, st.xp);
+}
+
+// k is a valid column (callers clamp it); every lane always loads
+template <int WF, bool XF32, int NR>
+MOE_DEV void up_load(UpStage<WF, XF32, NR>& st, const uint8_t* gb, const uint8_t* ub, const void* gs, const void* us,
+                     const void* x, int xrow, int H, int i0, int k) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    st.g[r] = *reinterpret_cast<const u32x4*>(gb + (size_t(r) * H + k) * Fmt<WF>::ES);
+    st.u[r] = *reinterpret_cast<const u32x4*>(ub + (size_t(r) * H + k) * Fmt<WF>::ES);
+  }
+  if constexpr (XF32) {
+    load_x<true, Fmt<WF>::EPL>(x, size_t(xrow) * H + k, st.x);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Fmt<WF>::EPL / 8; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + size_t(xrow) * H + k + 8 * i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st.xp[4 * i + q] = v[q];
+    }
+  }
+  if (WF == W_MXFP8) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      st.sg[r] = wscale<WF>(gs, i0 + r, k, H);
+      st.su[r] = wscale<WF>(us, i0 + r, k, H);
+    }
+  } else {
+    st.sg[0] = wscale<WF>(gs, i0, k, H);
+    st.su[0] = wscale<WF>(us, i0, k, H);
+  }
+}
+
+// adds the stage's partial products; lanes past the row end (valid false) add 0
+template <int WF, bool XF32, int NR>
+MOE_DEV void up_math(const UpStage<WF, XF32, NR>& st, bool valid, float (&ag)[NR], float (&au)[NR]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float sg = valid ? (WF == W_MXFP8 ? st.sg[r] : st.sg[0]) : 0.0f;
+    const float su = valid ? (WF == W_MXFP8 ? st.su[r] : st.su[0]) : 0.0f;
+    ag[r] = fmaf(up_dot<WF, XF32, NR>(st.g[r], st), sg, ag[r]);
+    au[r] = fmaf(up_dot<WF, XF32, NR>(st.u[r], st), su, au[r]);
+  }
+}
+
+// h[i0 .. i0+NR) = SiLU(x.Wg^T) * (x.Wu^T) for one x row.  NC chunks per
+// iteration: all their loads (NC x 2NR x 16 bytes per lane) are issued before
+// any is reduced, and no register stage is carried across iterations, so
+// nothing forces a wait on loads still in flight.
+template <int WF, bool XF32, int NR = RU, int NC = CPI>
 MOE_DEV void gate_up_item(const void* x, int H, int xrow, const void* g, const void* u, const void* gs,
-                          const void* us, int I, int i0, float* hrow) {
-  constexpr int EPL = Epl<WF>::v;
-  constexpr int CW = 64 * EPL;
+                          const void* us, int i0, float* hrow) {
+  constexpr int CW = Fmt<WF>::CW, EPL = Fmt<WF>::EPL;
   const int lane = lane_id();
-  float ag[RB] = {}, au[RB] = {};
-  const uint8_t* gb = static_cast<const uint8_t*>(g) + size_t(i0) * H * esize<WF>();
-  const uint8_t* ub = static_cast<const uint8_t*>(u) + size_t(i0) * H * esize<WF>();
-  for (int k = lane * EPL; k < H; k += CW) {
-    float xv[EPL];
-    load_x<XF32>(x, size_t(xrow) * H + k, xv, EPL);
-    uint4 wg[RB], wu[RB];
+  const uint8_t* gb = static_cast<const uint8_t*>(g) + size_t(i0) * H * Fmt<WF>::ES;
+  const uint8_t* ub = static_cast<const uint8_t*>(u) + size_t(i0) * H * Fmt<WF>::ES;
+  float ag[NR] = {}, au[NR] = {};
+  const int kl = lane * EPL;
+  for (int k0 = 0; k0 < H; k0 += NC * CW) {
+    UpStage<WF, XF32, NR> st[NC];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      wg[r] = *reinterpret_cast<const uint4*>(gb + (size_t(r) * H + k) * esize<WF>());
-      wu[r] = *reinterpret_cast<const uint4*>(ub + (size_t(r) * H + k) * esize<WF>());
-    }
-    if (WF == W_MXFP8) {
+    for (int c = 0; c < NC; ++c)
+      if (c == 0 || k0 + c * CW < H)  // uniform
+        up_load<WF, XF32, NR>(st[c], gb, ub, gs, us, x, xrow, H, i0, min(k0 + c * CW + kl, H - EPL));
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        ag[r] = fmaf(dot_chunk<WF>(wg[r], xv), wscale<WF>(gs, i0 + r, k, H), ag[r]);
-        au[r] = fmaf(dot_chunk<WF>(wu[r], xv), wscale<WF>(us, i0 + r, k, H), au[r]);
-      }
-    } else {
-      const float sg = wscale<WF>(gs, i0, k, H), su = wscale<WF>(us, i0, k, H);
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        ag[r] = fmaf(dot_chunk<WF>(wg[r], xv), sg, ag[r]);
-        au[r] = fmaf(dot_chunk<WF>(wu[r], xv), su, au[r]);
-      }
-    }
+    for (int c = 0; c < NC; ++c)
+      if (c == 0 || k0 + c * CW < H) up_math<WF, XF32, NR>(st[c], k0 + c * CW + kl < H, ag, au);
   }
   float mine = 0.f;
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    float gv = wave_sum(ag[r]);
-    float uv = wave_sum(au[r]);
+  for (int r = 0; r < NR; ++r) {
+    const float gv = wave_sum(ag[r]);
+    const float uv = wave_sum(au[r]);
     if (lane == r) mine = silu(gv) * uv;
   }
-  if (lane < RB) hrow[i0 + lane] = mine;
+  if (lane < NR) hrow[i0 + lane] = mine;
 }
 
 MOE_DEV int seg_of(const int* seg, int E, int r) {
-  int lo = 0, hi = E;  // find e with seg[e] <= r < seg[e+1]
+  int lo = 0, hi = E;  // e with seg[e] <= r < seg[e+1]
   while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
+    const int mid = (lo + hi) >> 1;
     if (seg[mid] <= r) lo = mid; else hi = mid;
   }
   return lo;
 }
 
-template <int WF, int SWF, bool XF32, bool XSF32>
-__global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvUpParams p) {
+template <int WF, int SWF, bool XF32, bool XSF32, int NR = RU, int NC = CPI>
+MOE_DEV void gemv_gate_up_kernel_body(const GemvUpParams& p) {
   const long wid = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int nslots = p.ids ? p.T * p.K : (p.seg ? p.T : 0);
-  const long nr = long(nslots) * (p.I / RB);
-  const long ns = p.hs ? long(p.T) * (p.Is / RB) : 0;
+  const long nr = long(nslots) * (p.I / NR);
+  const long ns = p.hs ? long(p.T) * (p.Is / NR) : 0;
   if (wid < nr) {
-    const int slot = int(wid / (p.I / RB)), i0 = int(wid % (p.I / RB)) * RB;
+    const int slot = int(wid / (p.I / NR)), i0 = int(wid % (p.I / NR)) * NR;
     int e, xrow;
     if (p.ids) {
       e = p.ids[slot];
@@ -154,93 +244,226 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvUpParams p) {
       e = seg_of(p.seg, p.E, slot);
       xrow = slot;
     }
-    const size_t wstride = size_t(p.I) * p.H * esize<WF>();
-    const size_t sstride = WF == W_FP8_B128 ? size_t(p.I / 128) * (p.H / 128) * 4
-                                            : (WF == W_MXFP8 ? size_t(p.I) * (p.H / 32) : 0);
-    gate_up_item<WF, XF32>(p.x, p.H, xrow, static_cast<const uint8_t*>(p.g) + e * wstride,
-                           static_cast<const uint8_t*>(p.u) + e * wstride,
-                           p.gs ? static_cast<const uint8_t*>(p.gs) + e * sstride : nullptr,
-                           p.us ? static_cast<const uint8_t*>(p.us) + e * sstride : nullptr, p.I, i0,
+    const size_t ws = wstride<WF>(p.I, p.H), ss = sstride<WF>(p.I, p.H);
+    gate_up_item<WF, XF32, NR, NC>(p.x, p.H, xrow, static_cast<const uint8_t*>(p.g) + e * ws,
+                           static_cast<const uint8_t*>(p.u) + e * ws,
+                           p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr,
+                           p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr, i0,
                            p.h + size_t(slot) * p.I);
   } else if (wid < nr + ns) {
     const long w2 = wid - nr;
-    const int t = int(w2 / (p.Is / RB)), i0 = int(w2 % (p.Is / RB)) * RB;
-    gate_up_item<SWF, XSF32>(p.xs, p.H, t, p.sg, p.su, p.sgs, p.sus, p.Is, i0, p.hs + size_t(t) * p.Is);
+    const int t = int(w2 / (p.Is / NR)), i0 = int(w2 % (p.Is / NR)) * NR;
+    gate_up_item<SWF, XSF32, NR, NC>(p.xs, p.H, t, p.sg, p.su, p.sgs, p.sus, i0, p.hs + size_t(t) * p.Is);
   }
 }
 
-// acc[r] += factor * sum_k W[n0+r][k] * h[k] over one [H][L] matrix
+template <int WF, int SWF, bool XF32, bool XSF32>
+__global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvUpParams p) {
+  gemv_gate_up_kernel_body<WF, SWF, XF32, XSF32>(p);
+}
+
+// ------------------------------------------------------------------ down
+
+// Where one lane's 16-byte chunk of the concatenated K lives.
+struct DownSrc {
+  const uint8_t* w;  // weight row n0 at this chunk's column
+  const float* h;    // activation at this chunk's column
+  const void* s;     // scale array of the matrix (null for bf16)
+  int L;             // row length of the matrix
+  int off;           // column within the matrix
+  float f;           // routing weight folded into the scale
+  bool ok;
+};
+
 template <int WF>
-MOE_DEV void down_segment(const void* W, const void* S, int L, const float* h, float factor, int n0,
-                          float (&acc)[RB]) {
-  constexpr int EPL = Epl<WF>::v;
-  constexpr int CW = 64 * EPL;
-  const int lane = lane_id();
-  const uint8_t* wb = static_cast<const uint8_t*>(W) + size_t(n0) * L * esize<WF>();
-  for (int k = lane * EPL; k < L; k += CW) {
-    float hv[EPL];
-    load_x<true>(h, k, hv, EPL);
-    uint4 w[RB];
+struct DownStage {
+  u32x4 w[RD];
+  float h[Fmt<WF>::EPL];
+  float sc[RD];
+};
+
+template <int WF>
+MOE_DEV void down_load(DownStage<WF>& st, const DownSrc& d, int n0) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) w[r] = *reinterpret_cast<const uint4*>(wb + (size_t(r) * L + k) * esize<WF>());
-    if (WF == W_MXFP8) {
+  for (int r = 0; r < RD; ++r) st.w[r] = *reinterpret_cast<const u32x4*>(d.w + size_t(r) * d.L * Fmt<WF>::ES);
+  load_x<true, Fmt<WF>::EPL>(d.h, 0, st.h);
+  if (WF == W_MXFP8) {
 #pragma unroll
-      for (int r = 0; r < RB; ++r) acc[r] = fmaf(dot_chunk<WF>(w[r], hv), factor * wscale<WF>(S, n0 + r, k, L), acc[r]);
-    } else {
-      const float f = factor * wscale<WF>(S, n0, k, L);
-#pragma unroll
-      for (int r = 0; r < RB; ++r) acc[r] = fmaf(dot_chunk<WF>(w[r], hv), f, acc[r]);
-    }
+    for (int r = 0; r < RD; ++r) st.sc[r] = d.f * wscale<WF>(d.s, n0 + r, d.off, d.L);
+  } else {
+    st.sc[0] = d.f * wscale<WF>(d.s, n0, d.off, d.L);
   }
 }
 
+// lanes whose chunk column lies past the end (ok false) add 0
 template <int WF>
-MOE_DEV size_t down_wstride(int H, int L) { return size_t(H) * L * esize<WF>(); }
+MOE_DEV void down_math(const DownStage<WF>& st, bool ok, float (&acc)[RD]) {
+#pragma unroll
+  for (int r = 0; r < RD; ++r) {
+    const float sc = ok ? (WF == W_MXFP8 ? st.sc[r] : st.sc[0]) : 0.0f;
+    acc[r] = fmaf(dot_chunk<WF>(st.w[r], st.h), sc, acc[r]);
+  }
+}
+
+// chunk c (global index over the routed part) of the concatenation of nseg
+// routed [H][I] matrices for this lane
+// sid/swt: the row's expert ids and routing weights staged in LDS
 template <int WF>
-MOE_DEV size_t down_sstride(int H, int L) {
-  return WF == W_FP8_B128 ? size_t(H / 128) * (L / 128) * 4 : (WF == W_MXFP8 ? size_t(H) * (L / 32) : 0);
+MOE_DEV DownSrc routed_src(const GemvDownParams& p, int row, int n0, int c, int nseg, float inv_i, const int* sid,
+                           const float* swt) {
+  DownSrc d{};
+  const int kraw = c * Fmt<WF>::CW + lane_id() * Fmt<WF>::EPL;
+  d.ok = kraw < nseg * p.I;
+  const int kc = min(kraw, nseg * p.I - Fmt<WF>::EPL);  // past the end: a valid column, masked later
+  int j = int(float(kc) * inv_i);                       // segment index without an integer division
+  j -= (j * p.I > kc);
+  j += ((j + 1) * p.I <= kc);
+  d.off = kc - j * p.I;
+  d.L = p.I;
+  const int e = sid[j];
+  const int hrow = nseg == 1 ? row : row * p.K + j;
+  d.f = swt[j];
+  d.w = static_cast<const uint8_t*>(p.d) + e * wstride<WF>(p.H, p.I) + (size_t(n0) * p.I + d.off) * Fmt<WF>::ES;
+  d.s = p.ds ? static_cast<const uint8_t*>(p.ds) + e * sstride<WF>(p.H, p.I) : nullptr;
+  d.h = p.h + size_t(hrow) * p.I + d.off;
+  return d;
+}
+
+template <int SWF>
+MOE_DEV DownSrc shared_src(const GemvDownParams& p, int row, int n0, int c) {
+  DownSrc d{};
+  const int kraw = c * Fmt<SWF>::CW + lane_id() * Fmt<SWF>::EPL;
+  d.ok = kraw < p.Is;
+  const int kc = min(kraw, p.Is - Fmt<SWF>::EPL);
+  d.off = kc;
+  d.L = p.Is;
+  d.f = 1.0f;
+  d.w = static_cast<const uint8_t*>(p.sd) + (size_t(n0) * p.Is + kc) * Fmt<SWF>::ES;
+  d.s = p.sds;
+  d.h = p.hs + size_t(row) * p.Is + kc;
+  return d;
+}
+
+// Stream this wave's chunks (c = first, first + step, ...) of one format, two
+// per iteration (both loads issued before either reduction); loop bounds are
+// uniform across the wave and loads are never predicated.
+template <int WF, class Src>
+MOE_DEV void down_stream(int first, int nchunks, int step, int n0, Src src, float (&acc)[RD]) {
+  for (int c = first; c < nchunks; c += 2 * step) {
+    DownStage<WF> sa, sb;
+    const bool two = c + step < nchunks;
+    const DownSrc da = src(c);
+    const DownSrc db = two ? src(c + step) : da;
+    down_load<WF>(sa, da, n0);
+    if (two) down_load<WF>(sb, db, n0);
+    down_math<WF>(sa, da.ok, acc);
+    if (two) down_math<WF>(sb, db.ok, acc);
+  }
 }
 
 template <int WF, int SWF>
 __global__ __launch_bounds__(256) void gemv_down_kernel(GemvDownParams p) {
-  const long wid = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int nb = p.H / RB;
-  const int nrows = p.out ? p.T : p.rows;
-  if (wid >= long(nrows) * nb) return;
-  const int row = int(wid / nb), n0 = int(wid % nb) * RB;
-  const int lane = lane_id();
-  float acc[RB] = {};
-  if (p.out) {  // combine mode: token `row`
-    for (int j = 0; j < p.K; ++j) {
-      const int e = p.ids[row * p.K + j];
-      down_segment<WF>(static_cast<const uint8_t*>(p.d) + e * down_wstride<WF>(p.H, p.I),
-                       p.ds ? static_cast<const uint8_t*>(p.ds) + e * down_sstride<WF>(p.H, p.I) : nullptr, p.I,
-                       p.h + size_t(row * p.K + j) * p.I, p.w[row * p.K + j], n0, acc);
-    }
-    if (p.hs) down_segment<SWF>(p.sd, p.sds, p.Is, p.hs + size_t(row) * p.Is, 1.0f, n0, acc);
-    uint32_t mine = 0;
+  __shared__ float part[DW][RD];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int nb = p.H / RD;
+  const int row = blockIdx.x / nb, n0 = (blockIdx.x % nb) * RD;
+  float acc[RD] = {};
+  const bool combine = p.out != nullptr;
+  // routed part: K segments (combine) or the row's own expert (per-row mode)
+  const bool routed = combine ? true : (p.seg != nullptr);
+  __shared__ int sid[16];
+  __shared__ float swt[16];
+  const int nseg = combine ? p.K : 1;
+  if (routed && threadIdx.x < nseg) {
+    sid[threadIdx.x] = combine ? p.ids[row * p.K + threadIdx.x] : seg_of(p.seg, p.E, row);
+    swt[threadIdx.x] = combine ? p.w[row * p.K + threadIdx.x] : 1.0f;
+  }
+  if (p.hs && (combine || p.seg == nullptr)) {  // the shared part needs no routing: start it first
+    const int nch = (p.Is + Fmt<SWF>::CW - 1) / Fmt<SWF>::CW;
+    down_stream<SWF>(wave, nch, DW, n0, [&](int c) { return shared_src<SWF>(p, row, n0, c); }, acc);
+  }
+  __syncthreads();
+  if (routed) {
+    const int nch = (nseg * p.I + Fmt<WF>::CW - 1) / Fmt<WF>::CW;
+    const float inv_i = 1.0f / float(p.I);
+    down_stream<WF>(wave, nch, DW, n0, [&](int c) { return routed_src<WF>(p, row, n0, c, nseg, inv_i, sid, swt); },
+                    acc);
+  }
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      float v = wave_sum(acc[r]);
-      if (lane == r) mine = f32_to_bf16(v);
-    }
-    if (lane < RB) p.out[size_t(row) * p.H + n0 + lane] = uint16_t(mine);
-  } else {  // per-row mode: y[row] = h[row] . Wd_e^T
-    if (p.seg) {
-      const int e = seg_of(p.seg, p.E, row);
-      down_segment<WF>(static_cast<const uint8_t*>(p.d) + e * down_wstride<WF>(p.H, p.I),
-                       p.ds ? static_cast<const uint8_t*>(p.ds) + e * down_sstride<WF>(p.H, p.I) : nullptr, p.I,
-                       p.h + size_t(row) * p.I, 1.0f, n0, acc);
+  for (int r = 0; r < RD; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == r) part[wave][r] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < RD) {
+    const int r = threadIdx.x;
+    float v = part[0][r];
+#pragma unroll
+    for (int w = 1; w < DW; ++w) v += part[w][r];
+    if (combine) {
+      if (p.ys_add) v += p.ys_add[size_t(row) * p.H + n0 + r];
+      p.out[size_t(row) * p.H + n0 + r] = f32_to_bf16(v);
     } else {
-      down_segment<SWF>(p.sd, p.sds, p.Is, p.hs + size_t(row) * p.Is, 1.0f, n0, acc);
+      p.y[size_t(row) * p.H + n0 + r] = v;
     }
-    float mine = 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ small-T stages
+
+// blocks [0, E): router logits of expert row blockIdx.x; the rest: shared
+// gate/up items (4 per block), which do not depend on the routing.
+template <int SWF, bool XSF32>
+__global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeParams p) {
+  __shared__ float part[4][kRouteGemvMaxT];
+  if (int(blockIdx.x) < p.rp.E) {
+    router_row(p.x, p.T, p.wr, p.rp, blockIdx.x, p.logits, part);
+    return;
+  }
+  const long wid = long(blockIdx.x - p.rp.E) * 4 + (threadIdx.x >> 6);
+  if (wid >= long(p.T) * (p.Is / RU)) return;
+  const int t = int(wid / (p.Is / RU)), i0 = int(wid % (p.Is / RU)) * RU;
+  gate_up_item<SWF, XSF32>(p.xs, p.H, t, p.sg, p.su, p.sgs, p.sus, i0, p.hs + size_t(t) * p.Is);
+}
+
+// block 0: top-k of every token (one wave each); the rest: shared down of
+// (token, 8 output rows) into ysh, split over the block's 4 waves.
+template <int SWF>
+__global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeParams p) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  if (blockIdx.x == 0) {
+    if (wave >= p.T) return;
+    const TopkLayout L(p.rp, lane);
+    float lg[kMpl];
+    topk_load(p.rp, L, p.logits + size_t(wave) * p.rp.E, p.bias, lg);
+    topk_select(p.rp, L, lg, p.ids + wave * p.rp.K, p.w + wave * p.rp.K);
+    return;
+  }
+  __shared__ float part[DW][RD];
+  const int nb = p.H / RD;
+  const int b = blockIdx.x - 1;
+  const int row = b / nb, n0 = (b % nb) * RD;
+  GemvDownParams d{};
+  d.H = p.H;
+  d.Is = p.Is;
+  d.hs = p.hs;
+  d.sd = p.sd;
+  d.sds = p.sds;
+  float acc[RD] = {};
+  const int nch = (p.Is + Fmt<SWF>::CW - 1) / Fmt<SWF>::CW;
+  down_stream<SWF>(wave, nch, DW, n0, [&](int c) { return shared_src<SWF>(d, row, n0, c); }, acc);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      float v = wave_sum(acc[r]);
-      if (lane == r) mine = v;
-    }
-    if (lane < RB) p.y[size_t(row) * p.H + n0 + lane] = mine;
+  for (int r = 0; r < RD; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == r) part[wave][r] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < RD) {
+    const int r = threadIdx.x;
+    float v = part[0][r];
+#pragma unroll
+    for (int w = 1; w < DW; ++w) v += part[w][r];
+    p.ysh[size_t(row) * p.H + n0 + r] = v;
   }
 }
 
@@ -278,9 +501,40 @@ hipError_t down_dispatch_s(const GemvDownParams& p, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_decode_stage1(const DecodeParams& p, hipStream_t s) {
+  const long items = p.Is ? long(p.T) * (p.Is / RU) : 0;
+  const dim3 grid(unsigned(p.rp.E + (items + 3) / 4));
+  const bool f = p.xs_f32;
+  switch (p.swfmt) {
+    case W_BF16:
+      if (f) hipLaunchKernelGGL((decode_stage1_kernel<W_BF16, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_stage1_kernel<W_BF16, false>), grid, dim3(256), 0, s, p);
+      break;
+    case W_FP8_B128:
+      if (f) hipLaunchKernelGGL((decode_stage1_kernel<W_FP8_B128, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_stage1_kernel<W_FP8_B128, false>), grid, dim3(256), 0, s, p);
+      break;
+    default:
+      if (f) hipLaunchKernelGGL((decode_stage1_kernel<W_MXFP8, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_stage1_kernel<W_MXFP8, false>), grid, dim3(256), 0, s, p);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_stage2(const DecodeParams& p, hipStream_t s) {
+  const dim3 grid(unsigned(1 + (p.Is ? p.T * (p.H / RD) : 0)));
+  switch (p.swfmt) {
+    case W_BF16: hipLaunchKernelGGL((decode_stage2_kernel<W_BF16>), grid, dim3(256), 0, s, p); break;
+    case W_FP8_B128: hipLaunchKernelGGL((decode_stage2_kernel<W_FP8_B128>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_stage2_kernel<W_MXFP8>), grid, dim3(256), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_gate_up(const GemvUpParams& p, hipStream_t s) {
   const int nslots = p.ids ? p.T * p.K : (p.seg ? p.T : 0);
-  const long items = long(nslots) * (p.I / RB) + (p.hs ? long(p.T) * (p.Is / RB) : 0);
+  const long items = long(nslots) * (p.I / RU) + (p.hs ? long(p.T) * (p.Is / RU) : 0);
   if (items == 0) return hipSuccess;
   const dim3 grid(unsigned((items + 3) / 4));
   switch (p.wfmt) {
@@ -292,13 +546,12 @@ hipError_t launch_gemv_gate_up(const GemvUpParams& p, hipStream_t s) {
 
 hipError_t launch_gemv_down(const GemvDownParams& p, hipStream_t s) {
   const int nrows = p.out ? p.T : p.rows;
-  const long items = long(nrows) * (p.H / RB);
-  if (items == 0) return hipSuccess;
-  const dim3 grid(unsigned((items + 3) / 4));
+  const long blocks = long(nrows) * (p.H / RD);
+  if (blocks == 0) return hipSuccess;
   switch (p.wfmt) {
-    case W_BF16: return down_dispatch_s<W_BF16>(p, grid, s);
-    case W_FP8_B128: return down_dispatch_s<W_FP8_B128>(p, grid, s);
-    default: return down_dispatch_s<W_MXFP8>(p, grid, s);
+    case W_BF16: return down_dispatch_s<W_BF16>(p, dim3(unsigned(blocks)), s);
+    case W_FP8_B128: return down_dispatch_s<W_FP8_B128>(p, dim3(unsigned(blocks)), s);
+    default: return down_dispatch_s<W_MXFP8>(p, dim3(unsigned(blocks)), s);
   }
 }
 

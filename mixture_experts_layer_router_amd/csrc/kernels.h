@@ -14,12 +14,10 @@ struct RouteParams {
   int H, E, G, TG, K;
   float scale;
 };
-// Small-T router: GEMV over the E rows spread over the grid, then the last
-// workgroup to finish runs the top-k for every token.  T <= kRouteGemvMaxT.
+// Small-T router logits: one workgroup per expert row.  T <= kRouteGemvMaxT.
 constexpr int kRouteGemvMaxT = 4;
-hipError_t launch_route_gemv_topk(const uint16_t* x, int T, const uint16_t* wr, const float* bias,
-                                  const RouteParams& p, float* logits_ws, unsigned* counter_ws,
-                                  int* ids, float* w, hipStream_t s);
+hipError_t launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const RouteParams& p,
+                               float* logits, hipStream_t s);
 // Top-k over precomputed fp32 logits [T][E] (bias added here).
 hipError_t launch_topk(const float* logits, int T, const float* bias, const RouteParams& p, int* ids,
                        float* w, hipStream_t s);
@@ -123,8 +121,36 @@ struct GemvDownParams {
   int rows;
   const int* seg;
   int E;
+  const float* ys_add;  // combine mode: fp32 [T][H] added before the rounding (shared output), or null
 };
 hipError_t launch_gemv_down(const GemvDownParams& p, hipStream_t s);
+
+// Small-T layer in four launches whose dependencies are hidden behind
+// independent work (no device-wide synchronisation inside a launch):
+//   stage 1: router logits || shared gate/up
+//   stage 2: top-k || shared down (-> ysh)
+//   then routed gate/up (launch_gemv_gate_up) and routed down + combine
+//   (launch_gemv_down with ys_add = ysh).
+struct DecodeParams {
+  const uint16_t* x;  // bf16 [T][H] (router input)
+  int T, H;
+  const uint16_t* wr;
+  const float* bias;
+  RouteParams rp;
+  float* logits;  // [T][E]
+  int* ids;       // [T][K]
+  float* w;       // [T][K]
+  // shared expert (Is = 0: none)
+  int swfmt;
+  const void* xs;  // shared-expert input: bf16 or fp32 dequantised
+  bool xs_f32;
+  const void *sg, *su, *sgs, *sus, *sd, *sds;
+  int Is;
+  float* hs;   // fp32 [T][Is]
+  float* ysh;  // fp32 [T][H]
+};
+hipError_t launch_decode_stage1(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_stage2(const DecodeParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ combine
 // out[t] = bf16(sum_j w[t][j] * y_perm[inv_pos[t*K+j]] + y_shared[t]).

@@ -1,0 +1,169 @@
+// Device-side routing pieces shared by the router kernels: the small-T router
+// GEMV row and the per-token group-limited greedy top-k (stage O of the
+// DSV2-236B-MegaKernel README flowchart).
+#pragma once
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr float kNegInfF = -INFINITY;
+
+MOE_DEV int wave_min_i(int v) {
+  auto step = [](int a, int b) { return a < b ? a : b; };
+  v = step(v, __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false));
+  v = step(v, __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false));
+  v = step(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));
+  v = step(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));
+  v = step(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));
+  v = step(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// max over aligned groups of `lpg` lanes (lpg a power of two <= 64); every lane
+// of a group gets the group's value
+MOE_DEV float lanes_max(float v, int lpg) {
+  if (lpg >= 2) v = fmaxf(v, dpp_f<0xb1>(v, v));
+  if (lpg >= 4) v = fmaxf(v, dpp_f<0x4e>(v, v));
+  if (lpg >= 8) v = fmaxf(v, dpp_f<0x141>(v, v));
+  if (lpg >= 16) v = fmaxf(v, dpp_f<0x140>(v, v));
+  if (lpg >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if (lpg >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Lane layout of one token's logits: groups of gsz contiguous experts, each
+// group spread over lpg = 64 / next_pow2(G) lanes; lane l holds members
+// (l % lpg) + lpg*j of group l / lpg, j < kMpl.  E <= 256 gives at most 8.
+constexpr int kMpl = 8;
+struct TopkLayout {
+  int gsz, lpg, g, m0;
+  MOE_DEV TopkLayout(const RouteParams& p, int lane) {
+    gsz = p.E / p.G;
+    int gp = 1;
+    while (gp < p.G) gp <<= 1;
+    lpg = 64 / gp;
+    g = lane / lpg;
+    m0 = lane % lpg;
+  }
+  // expert id of slot j, or -1
+  MOE_DEV int expert(const RouteParams& p, int j) const {
+    const int m = m0 + lpg * j;
+    return (g < p.G && m < gsz) ? g * gsz + m : -1;
+  }
+};
+
+// One wave routes one token.  lg[j]: logit (bias included) of layout slot j,
+// -inf for empty slots.  Writes ids[0..K) and w[0..K) (lane 0).
+//   softmax over all experts; group score = max member; top-TG groups by
+//   rank (ties to the lower group); then K rounds of (largest logit among the
+//   kept groups' experts, ties to the lower id).  w = scale * softmax score.
+MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[kMpl], int* ids, float* w) {
+  const int lane = lane_id();
+  float mx = kNegInfF;
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) mx = fmaxf(mx, lg[j]);
+  const float gmax = lanes_max(mx, L.lpg);  // this lane's group maximum
+  const float m = wave_max(mx);
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j)
+    if (lg[j] != kNegInfF) se += expf(lg[j] - m);
+  const float s = wave_sum(se);
+  // rank of this lane's group among the G group maxima
+  int grank = 0;
+  for (int q = 0; q < p.G; ++q) {
+    const float o = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gmax), q * L.lpg));
+    grank += (o > gmax) || (o == gmax && q < L.g);
+  }
+  const bool kept = L.g < p.G && grank < p.TG;
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j)
+    if (!kept) lg[j] = kNegInfF;
+  for (int r = 0; r < p.K; ++r) {
+    float best = kNegInfF;
+    int bj = 0;
+#pragma unroll
+    for (int j = 0; j < kMpl; ++j)
+      if (lg[j] > best) {  // strict: the lower slot (lower id) wins ties
+        best = lg[j];
+        bj = j;
+      }
+    const float v = wave_max(best);
+    const int mine = (best == v && best != kNegInfF) ? L.expert(p, bj) : 0x7fffffff;
+    const int e = wave_min_i(mine);
+    if (mine == e) {
+#pragma unroll
+      for (int j = 0; j < kMpl; ++j)
+        if (j == bj) lg[j] = kNegInfF;
+    }
+    if (lane == 0) {
+      ids[r] = e;
+      w[r] = p.scale * (expf(v - m) / s);
+    }
+  }
+}
+
+// Router logits of one expert row e for T <= kRouteGemvMaxT tokens, computed
+// by one workgroup of 256 threads: all of the row's 16-byte loads are issued
+// before any arithmetic; partial sums meet in `part` (LDS) in wave order.
+MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* __restrict__ wr, const RouteParams& p,
+                        int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint16_t* row = wr + size_t(e) * p.H;
+  float acc[kRouteGemvMaxT] = {};
+  // 256 threads x 8 bf16 = 2048 columns per pass; 4 passes issued together
+  for (int k0 = 0; k0 < p.H; k0 += 4 * 2048) {
+    u32x4 wv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = min(k0 + c * 2048 + tid * 8, p.H - 8);
+      wv[c] = *reinterpret_cast<const u32x4*>(row + k);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int kraw = k0 + c * 2048 + tid * 8;
+      const int k = min(kraw, p.H - 8);
+      const float on = kraw < p.H ? 1.0f : 0.0f;
+#pragma unroll
+      for (int t = 0; t < kRouteGemvMaxT; ++t) {
+        if (t < T) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(x + size_t(t) * p.H + k);
+          float a = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(wv[c][q] << 16), a);
+            a = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[c][q] & 0xffff0000u), a);
+          }
+          acc[t] = fmaf(a, on, acc[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouteGemvMaxT; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (lane == 0) part[wave][t] = v;
+  }
+  __syncthreads();
+  if (tid < T) logits[tid * p.E + e] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+}
+
+// Load one token's logits (+ bias) into the layout.
+MOE_DEV void topk_load(const RouteParams& p, const TopkLayout& L, const float* logits_row, const float* bias,
+                       float (&lg)[kMpl]) {
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) {
+    const int e = L.expert(p, j);
+    float v = kNegInfF;
+    if (e >= 0) {
+      v = logits_row[e];
+      if (bias) v += bias[e];
+    }
+    lg[j] = v;
+  }
+}
+
+}  // namespace moe

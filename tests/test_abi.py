@@ -17,7 +17,7 @@ OK, EINVAL, EUNSUP, EALIGN, EWS = 0, 1, 2, 3, 4
 
 def declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^(?:moe_status|const char\*|int32_t)\s+(moe_\w+)\s*\(", src, re.M)))
 
 
 def test_exports_every_declared_symbol():

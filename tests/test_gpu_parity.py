@@ -42,6 +42,13 @@ SMALL = {
     "flat_k1_64tok": small_cfg(0, tokens=64, n_experts=8, n_groups=1, topk_groups=1, topk=1, shared_inter=0),
     "one_group_32tok": small_cfg(2, tokens=32, hidden=256, n_experts=16, n_groups=4, topk_groups=1, topk=2,
                                  inter=128, shared_inter=128),
+    # small T: the decode path (router || shared gate/up, top-k || shared down)
+    "b128_quant_2tok": small_cfg(2, tokens=2, hidden=384, n_experts=16, n_groups=4, topk_groups=2, topk=3,
+                                 inter=256, shared_inter=256),
+    "mx_3tok": small_cfg(3, tokens=3, hidden=512, n_experts=8, inter=256, shared_inter=256),
+    "bf16_1tok": small_cfg(0, tokens=1),
+    "b128_4tok_noshared": small_cfg(1, tokens=4, hidden=256, n_experts=12, n_groups=3, topk_groups=2, topk=2,
+                                    inter=128, shared_inter=0),
 }
 
 
