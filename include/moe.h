@@ -27,9 +27,11 @@
  *   MOE_EHIP; faults inside kernels surface at the caller's next sync.
  * - The caller owns all memory.  The library never allocates.  Calls that
  *   take a workspace need `ws_bytes` >= moe_workspace_size(); the workspace
- *   must be zero-filled once before its first use (torch.zeros is enough)
- *   and is left reusable by every call.  Calls sharing one workspace must
- *   be ordered on one stream.
+ *   must be zero-filled once before its first use (torch.zeros is enough):
+ *   its first 32 KiB hold the work queues and counters of moe_forward's
+ *   single-launch path, which every call leaves zero again.  Calls sharing
+ *   one workspace must be ordered on one stream; overlapping calls on one
+ *   workspace race.
  * - Status codes: nothing is thrown across the ABI.  Host-side validation
  *   runs before any launch, so a failed check launches nothing.
  *     MOE_EINVAL        null pointer, T < 0, hidden/inter <= 0,
@@ -179,7 +181,20 @@ moe_status moe_combine(const moe_config* cfg /*host*/, const float* y_perm, cons
 /* The whole layer: route, dispatch, routed and shared FFNs, combine.
  * out bf16 [T][H].  topk_ids_out int32 [T][K] and topk_w_out fp32 [T][K]
  * may be NULL.  Numerics depend only on cfg: every path honours the same
- * activation format. */
+ * activation format.
+ * Paths: T <= 4 with both activation formats MOE_A_NONE and one weight
+ * format for routed and shared experts runs as ONE
+ * persistent launch (the DSV2-236B-MegaKernel README's single-launch idea,
+ * "What runs inside the single launch"): workgroups take router rows,
+ * shared gate/up, routed gate/up and down+combine items in that order from
+ * queues in the workspace, and wait (bounded) only for earlier items.
+ * Waits give up after about 0.2 s: int32 word 0 of the workspace then
+ * becomes nonzero (sticky) and the rows of `out` written by the workgroup
+ * that gave up are NaN.  With the device to itself a wait lasts microseconds;
+ * the queue order keeps the launch free of deadlock whatever number of its
+ * workgroups are resident (at least 32).  Other T <= 4 cases run
+ * in four to six launches, T <= 4 never needs more; larger T runs the
+ * dispatch + grouped-GEMM path (or the GEMV path for formats it lacks). */
 moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
                        const uint16_t* w_router, const float* bias,
                        const moe_ffn_weights* routed /*host struct*/,

@@ -22,12 +22,14 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// test hook: MOE_FORCE_PATH=gemv|gemm
+// test hook: MOE_FORCE_PATH=gemv|gemm|staged (staged: the GEMV path with the
+// small-T layer in separate launches instead of the single-launch kernel)
 int forced_path() {
   const char* s = getenv("MOE_FORCE_PATH");
   if (!s) return 0;
   if (!strcmp(s, "gemv")) return 1;
   if (!strcmp(s, "gemm")) return 2;
+  if (!strcmp(s, "staged")) return 3;
   return 0;
 }
 
@@ -104,7 +106,7 @@ Ws plan(const moe_config* c, int Tm) {
     o += up(std::max<size_t>(bytes, 16));
     return at;
   };
-  s.counter = take(256);
+  s.counter = take(kFusedCtrBytes);  // must stay at offset 0 (documented in moe.h)
   s.logits = take(T * E * 4);
   s.ids = take(TK * 4);
   s.w = take(TK * 4);
@@ -446,7 +448,40 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   const int fp = forced_path();
   const bool pairs_ok = gemm_pair(cfg->routed_wfmt, raf) && (!has_shared || gemm_pair(cfg->shared_wfmt, saf));
   if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
-  const bool gemv = fp == 1 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
+  const bool gemv = fp == 1 || fp == 3 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
+
+  if (gemv && T <= kRouteGemvMaxT && fp != 3 && raf == A_NONE &&
+      (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt))) {
+    // small T, bf16 activations: the whole layer in one persistent launch
+    FusedDecodeParams fp_{};
+    DecodeParams& dp = fp_.d;
+    dp.x = x;
+    dp.T = T;
+    dp.H = H;
+    dp.wr = w_router;
+    dp.bias = bias;
+    dp.rp = route_params(cfg);
+    dp.logits = at<float>(ws, L.logits);
+    dp.ids = ids;
+    dp.w = w;
+    dp.swfmt = has_shared ? cfg->shared_wfmt : W_BF16;
+    if (has_shared) {
+      dp.xs = x;
+      dp.sg = shared->gate; dp.su = shared->up; dp.sgs = shared->gate_s; dp.sus = shared->up_s;
+      dp.sd = shared->down; dp.sds = shared->down_s;
+      dp.Is = cfg->shared_inter;
+      dp.hs = at<float>(ws, L.hsh);
+    }
+    fp_.wfmt = cfg->routed_wfmt;
+    fp_.I = cfg->inter;
+    fp_.g = routed->gate; fp_.u = routed->up; fp_.gs = routed->gate_s; fp_.us = routed->up_s;
+    fp_.dn = routed->down; fp_.dns = routed->down_s;
+    fp_.h = at<float>(ws, L.h);
+    fp_.out = out;
+    fp_.ctr = at<unsigned>(ws, L.counter);
+    LAUNCH("decode_fused", launch_fused_decode(fp_, stream));
+    return MOE_OK;
+  }
 
   if (gemv && T <= kRouteGemvMaxT) {
     // small T: router || shared gate/up, then top-k || shared down, then the

@@ -1,0 +1,363 @@
+// Single-launch small-batch MoE layer (T <= 4, bf16 activations, one weight
+// format for routed and shared experts): stages N, O, P1/Q1, P2/Q2 and the
+// sum of R of the DSV2-236B-MegaKernel README flowchart in one persistent
+// launch, so HBM keeps streaming weights across what would otherwise be four
+// kernel boundaries (each costs a ramp and a tail of a few microseconds).
+//
+// Router rows come first: workgroup e < E computes row e of the logits
+// (all tokens) as soon as it starts; the lowest block indices are dispatched
+// first, and the routing is what every routed item waits for.  The rest of
+// the work is a list of items in dependency order:
+//   SU  shared gate/up         (8 intermediate columns of one token)
+//   RG  routed gate/up         (8 intermediate columns of one (token, slot))
+//   DN  down + combine         (4 output rows of one token: the shared and
+//                               the K routed down matrices as one long dot)
+// RG needs all router rows (each workgroup runs the top-k itself from the
+// logits); DN needs the routing for its weight addresses and SU + RG for h.
+// A DN item issues its weight loads first and only then waits for h, so the
+// down weights stream while the last gate/up items finish.  Item i sits in
+// queue i % kQ; workgroup b takes the items of queue b % kQ in order with one
+// atomic each.  An item waits only for the router rows (which wait for
+// nothing) or for earlier items, and a queue hands out its items in order, so
+// the earliest unfinished item is always held by a running workgroup or about
+// to be taken by one: the launch completes whatever the number of resident
+// workgroups (at least max(E, kQ): the router rows' workgroups are the first
+// dispatched).
+//
+// Same-address device-scope atomics serialise at about 12 ns each, so a
+// workgroup counts its finished items of a phase in a register and adds them
+// to the phase's counter in one atomic when its run of items of that phase
+// ends (its next item belongs to another phase, or there is none); whoever
+// brings the counter to the phase's item count raises the phase's ready flag.
+// Waiters poll only the flag (a line no atomic touches).  A workgroup never
+// waits while it holds uncounted items, so nothing waits on itself.
+// Cross-workgroup data (logits, ids / weights, h) is written with
+// device-scope atomic stores; a producer waits for its stores (vmcnt(0))
+// before its increment.  A consumer reads the data with plain loads after
+// seeing the flag: its XCD's L2 cannot hold those lines yet, since nothing
+// reads them before the flag rises and every launch starts with clean L2s.
+// No L2 writeback or invalidate is needed.  Waits are bounded (about 0.2 s):
+// a wait that gives up sets the error word and the workgroup writes NaN for
+// its outputs.  The last workgroup to exit resets every counter and flag.
+#include <algorithm>
+
+#include "gemv_dev.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kQ = 32;         // queues, and most stripes of a counter
+constexpr int kLine = 32;      // words per 128-byte line
+constexpr int kUR = 2;         // intermediate columns per wave in a gate/up item
+constexpr int kURP = 1;        // ... computed per pass (2 * kURP weight rows in flight)
+constexpr int kUC = 3;         // weight chunks per row loaded together in a gate/up pass
+constexpr int kUpCols = 4 * kUR;
+constexpr int kDR = 4;         // output rows of a down item
+constexpr int kDJ = 3;         // down chunks per wave held in registers at once
+constexpr int kPhases = 3;     // phases that signal completion: R, SU, RG
+constexpr uint64_t kWaitTicks = 20000000;  // s_memrealtime runs at 100 MHz: 0.2 s
+
+// Counter block (one counter per 128-byte line, word 0 of the line):
+//   line 0: error word                     lines 1..kQ: queue heads
+//   per phase f: item counter, ready flag
+//   exit stripes (kQ) and exit summary
+struct Ctr {
+  unsigned* base;
+  MOE_DEV unsigned* error() const { return base; }
+  MOE_DEV unsigned* head(int q) const { return base + (1 + q) * kLine; }
+  MOE_DEV unsigned* count(int f) const { return base + (1 + kQ + 2 * f) * kLine; }
+  MOE_DEV unsigned* flag(int f) const { return base + (2 + kQ + 2 * f) * kLine; }
+  MOE_DEV unsigned* exit_stripe(int s) const { return base + (1 + kQ + 2 * kPhases + s) * kLine; }
+  MOE_DEV unsigned* exit_summary() const { return exit_stripe(kQ); }
+};
+constexpr int kCtrLines = 1 + kQ + 2 * kPhases + kQ + 1;
+static_assert(kCtrLines * kLine * 4 <= kFusedCtrBytes, "counter block");
+static_assert(kFusedErrorWord == 0, "error word");
+
+MOE_DEV unsigned atomic_add(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV unsigned atomic_inc(unsigned* p) { return atomic_add(p, 1u); }
+template <class V>
+MOE_DEV void store_agent(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// waits for completion of this thread's earlier global stores; the memory
+// clobber keeps the compiler from moving any store past it
+MOE_DEV void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Counts `cnt` finished items of phase f (of n).  Every thread calls it; the
+// workgroup's stores are complete before thread 0 counts the items.
+MOE_DEV void count_items(const Ctr& c, int f, int cnt, int n) {
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    if (atomic_add(c.count(f), unsigned(cnt)) + unsigned(cnt) == unsigned(n)) store_agent(c.flag(f), 1u);
+}
+
+// Bounded wait for phase f's ready flag; false if it gave up.
+MOE_DEV bool wait_flag(const Ctr& c, int f, int* s_ok) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if (__hip_atomic_load(c.flag(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(c.flag(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+          store_agent(c.error(), 1u);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    *s_ok = ok;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// sum of the 4 waves' partial row sums; thread r < R gets row r
+template <int R>
+MOE_DEV float rows_reduce(float (&acc)[R], float (*dpart)[kDR], int wave, int lane) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == r) dpart[wave][r] = v;
+  }
+  __syncthreads();
+  float v = 0.f;
+  if (threadIdx.x < R) {
+    v = dpart[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += dpart[w][threadIdx.x];
+  }
+  return v;
+}
+
+// Weights (and scales, with the routing weight folded in) of one down chunk
+// for kDR rows; the activations are loaded later, when they exist.
+template <int WF>
+struct DnStage {
+  u32x4 w[kDR];
+  float sc[WF == W_MXFP8 ? kDR : 1];
+};
+
+template <int WF>
+MOE_DEV void dn_load_w(DnStage<WF>& st, const DownSrc& s, int n0) {
+#pragma unroll
+  for (int r = 0; r < kDR; ++r) st.w[r] = *reinterpret_cast<const u32x4*>(s.w + size_t(r) * s.L * Fmt<WF>::ES);
+  if (WF == W_MXFP8) {
+#pragma unroll
+    for (int r = 0; r < kDR; ++r) st.sc[r] = s.f * wscale<WF>(s.s, n0 + r, s.off, s.L);
+  } else {
+    st.sc[0] = s.f * wscale<WF>(s.s, n0, s.off, s.L);
+  }
+}
+
+// lanes whose chunk column lies past the end (ok false) add 0
+template <int WF>
+MOE_DEV void dn_math(const DnStage<WF>& st, const DownSrc& s, float (&acc)[kDR]) {
+  float h[Fmt<WF>::EPL];
+  load_x<true, Fmt<WF>::EPL>(s.h, 0, h);
+#pragma unroll
+  for (int r = 0; r < kDR; ++r) {
+    const float sc = s.ok ? st.sc[WF == W_MXFP8 ? r : 0] : 0.0f;
+    acc[r] = fmaf(dot_chunk<WF>(st.w[r], h), sc, acc[r]);
+  }
+}
+
+template <int WF>
+__global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) {
+  __shared__ float part[4][kRouteGemvMaxT];
+  __shared__ float dpart[4][kDR];
+  __shared__ int sids[kRouteGemvMaxT * 16];
+  __shared__ float sw[kRouteGemvMaxT * 16];
+  __shared__ unsigned s_next;
+  __shared__ int s_ok, s_last;
+  const DecodeParams& d = p.d;
+  const Ctr c{p.ctr};
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int T = d.T, H = d.H, K = d.rp.K, E = d.rp.E, I = p.I, Is = d.Is;
+  const int n[4] = {E, Is ? T * (Is / kUpCols) : 0, T * K * (I / kUpCols), T * (H / kDR)};
+  const int b1 = 0, b2 = b1 + n[1], b3 = b2 + n[2];  // queue items: SU, RG, DN (R is static)
+  const unsigned total = unsigned(b3 + n[3]);
+  const int q = blockIdx.x % kQ;
+  // per-workgroup state (uniform across the workgroup)
+  bool have_r = false, have_topk = false, have_dn_deps = false, poisoned = false;
+  int pend_f = 0, pend_n = 0;  // finished items of phase pend_f not yet counted
+  auto phase_of = [&](int i) { return i < b2 ? 1 : (i < b3 ? 2 : 3); };
+
+  // R: workgroup e < E computes router row e before it joins the queues (the
+  // lowest block indices are dispatched first, so the routing, which every
+  // routed item waits for, starts at once)
+  if (int(blockIdx.x) < E) {
+    if (tid == 0) s_next = q + kQ * atomic_inc(c.head(q));
+    router_row(d.x, T, d.wr, d.rp, blockIdx.x, d.logits, part, true);
+    count_items(c, 0, 1, E);
+  } else if (tid == 0) {
+    s_next = q + kQ * atomic_inc(c.head(q));
+  }
+  __syncthreads();
+  unsigned item = s_next, next = 0;
+  while (item < total) {
+    // claim the next item now; its value is only needed (and waited for) when
+    // it is handed to the workgroup at the end of this one
+    if (tid == 0) next = atomic_inc(c.head(q));
+    const int it = int(item);
+    if (it < b2) {  // SU: 8 shared intermediate columns of one token
+      const int i = it - b1, per = Is / kUpCols;
+      const int t = i / per, c0 = (i % per) * kUpCols + wave * kUR;
+#pragma unroll 1
+      for (int u = 0; u < kUR; u += kURP)
+        gate_up_item<WF, false, kURP, kUC, true>(d.x, H, t, d.sg, d.su, d.sgs, d.sus, c0 + u, d.hs + size_t(t) * Is);
+    } else {
+      if (!have_topk) {  // every workgroup routes all T tokens itself (wave t: token t)
+        if (!have_r) {
+          poisoned |= !wait_flag(c, 0, &s_ok);
+          have_r = true;
+        }
+        if (wave < T) {
+          const TopkLayout L(d.rp, lane);
+          float lg[kMpl];
+          topk_load(d.rp, L, d.logits + size_t(wave) * E, d.bias, lg);
+          topk_select(d.rp, L, lg, sids + wave * K, sw + wave * K);
+        }
+        __syncthreads();
+        have_topk = true;
+      }
+      if (it < b3) {  // RG: 8 routed intermediate columns of one (token, slot)
+        const int i = it - b2;
+        if (i == 0 && tid < T * K) {  // one workgroup publishes the routing
+          store_agent(d.ids + tid, sids[tid]);
+          store_agent(d.w + tid, sw[tid]);
+        }
+        const int per = I / kUpCols;
+        const int slot = i / per, c0 = (i % per) * kUpCols + wave * kUR;
+        const int e = min(max(sids[slot], 0), E - 1);
+        const size_t ws = wstride<WF>(I, H), ss = sstride<WF>(I, H);
+        const uint8_t* ge = static_cast<const uint8_t*>(p.g) + e * ws;
+        const uint8_t* ue = static_cast<const uint8_t*>(p.u) + e * ws;
+        const uint8_t* gse = p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr;
+        const uint8_t* use = p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr;
+#pragma unroll 1
+        for (int u = 0; u < kUR; u += kURP)
+          gate_up_item<WF, false, kURP, kUC, true>(d.x, H, slot / K, ge, ue, gse, use, c0 + u, p.h + size_t(slot) * I);
+      } else {  // DN: kDR output rows of one token over [shared Is | routed K*I]
+        const int i = it - b3, nb = H / kDR;
+        const int t = i / nb, n0 = (i % nb) * kDR;
+        GemvDownParams g{};
+        g.H = H;
+        g.K = K;
+        g.I = I;
+        g.Is = Is;
+        g.h = p.h;
+        g.hs = d.hs;
+        g.d = p.dn;
+        g.ds = p.dns;
+        g.sd = d.sd;
+        g.sds = d.sds;
+        constexpr int CW = Fmt<WF>::CW;
+        const int nsh = (Is + CW - 1) / CW, ntot = nsh + (K * I + CW - 1) / CW;
+        const float inv_i = 1.0f / float(I);
+        const int* sid = sids + t * K;
+        const float* swt = sw + t * K;
+        auto src = [&](int ch) {
+          const int cc = min(ch, ntot - 1);
+          DownSrc s = cc < nsh ? shared_src<WF>(g, t, n0, cc) : routed_src<WF>(g, t, n0, cc - nsh, K, inv_i, sid, swt);
+          s.ok = s.ok && ch < ntot;
+          return s;
+        };
+        float acc[kDR] = {};
+        {  // this wave's first kDJ chunks: weights in flight before the wait for h
+          DnStage<WF> st[kDJ];
+          DownSrc s[kDJ];
+#pragma unroll
+          for (int j = 0; j < kDJ; ++j) {
+            s[j] = src(wave + 4 * j);
+            dn_load_w<WF>(st[j], s[j], n0);
+          }
+          if (!have_dn_deps) {
+            if (Is) poisoned |= !wait_flag(c, 1, &s_ok);
+            poisoned |= !wait_flag(c, 2, &s_ok);
+            have_dn_deps = true;
+          }
+#pragma unroll
+          for (int j = 0; j < kDJ; ++j) dn_math<WF>(st[j], s[j], acc);
+        }
+        for (int c0 = wave + 4 * kDJ; c0 < ntot; c0 += 4 * kDJ) {  // the rest, if any (no barrier inside)
+          DnStage<WF> st[kDJ];
+          DownSrc s[kDJ];
+#pragma unroll
+          for (int j = 0; j < kDJ; ++j) {
+            s[j] = src(c0 + 4 * j);
+            dn_load_w<WF>(st[j], s[j], n0);
+          }
+#pragma unroll
+          for (int j = 0; j < kDJ; ++j) dn_math<WF>(st[j], s[j], acc);
+        }
+        const float v = rows_reduce<kDR>(acc, dpart, wave, lane);
+        if (tid < kDR) p.out[size_t(t) * H + n0 + tid] = poisoned ? uint16_t(0x7fc0) : f32_to_bf16(v);
+      }
+    }
+    const int f = phase_of(it);
+    if (f == 1 || f == 2) {
+      pend_f = f;
+      ++pend_n;
+    }
+    if (tid == 0) s_next = q + kQ * next;
+    __syncthreads();
+    item = s_next;
+    __syncthreads();  // s_next is rewritten only after every thread has read it
+    if (pend_n && (item >= total || phase_of(int(item)) != pend_f)) {  // end of a run: count it
+      count_items(c, pend_f, pend_n, n[pend_f]);
+      pend_n = 0;
+    }
+  }
+  // exit count; the last workgroup out resets the counter block
+  if (tid == 0) {
+    const int G = int(gridDim.x), s = blockIdx.x % kQ;
+    const unsigned cnt = unsigned(G / kQ + (s < G % kQ));
+    int last = 0;
+    if (atomic_inc(c.exit_stripe(s)) + 1 == cnt) last = atomic_inc(c.exit_summary()) + 1 == unsigned(min(G, kQ));
+    s_last = last;
+  }
+  __syncthreads();
+  if (s_last)
+    for (int l = 1 + tid; l < kCtrLines; l += 256) store_agent(c.base + l * kLine, 0u);
+}
+
+template <int WF>
+hipError_t launch_fused(const FusedDecodeParams& p, hipStream_t s) {
+  // resident capacity of the device (more workgroups would only queue)
+  static int grid_for_dev[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int grid = dev < 64 ? grid_for_dev[dev] : 0;
+  if (grid == 0) {
+    int per_cu = 0, cus = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<WF>, 256, 0)) != hipSuccess)
+      return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    grid = std::max(std::max(per_cu, 1) * cus, kQ);
+    if (dev < 64) grid_for_dev[dev] = grid;
+  }
+  grid = std::max(grid, p.d.rp.E);  // one workgroup per router row
+  hipLaunchKernelGGL((fused_decode_kernel<WF>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s) {
+  if (p.d.Is && p.d.swfmt != p.wfmt) return hipErrorInvalidValue;
+  switch (p.wfmt) {
+    case W_BF16: return launch_fused<W_BF16>(p, s);
+    case W_FP8_B128: return launch_fused<W_FP8_B128>(p, s);
+    default: return launch_fused<W_MXFP8>(p, s);
+  }
+}
+
+}  // namespace moe

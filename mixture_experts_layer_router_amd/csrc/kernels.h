@@ -152,6 +152,24 @@ struct DecodeParams {
 hipError_t launch_decode_stage1(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_stage2(const DecodeParams& p, hipStream_t s);
 
+// Small-T layer with bf16 activations and one weight format for routed and
+// shared experts, in one persistent launch (decode.hip): router, top-k, shared
+// and routed gate/up, down + combine, ordered by work queues and completion
+// counters in `ctr` (kFusedCtrBytes, zero before the first launch; every
+// launch leaves it zero again, except the sticky error word).  d.xs must be
+// d.x (bf16); d.swfmt must equal wfmt; d.ysh is unused.
+struct FusedDecodeParams {
+  DecodeParams d;
+  int wfmt, I;
+  const void *g, *u, *gs, *us, *dn, *dns;  // routed experts
+  float* h;        // fp32 [T*K][I]
+  uint16_t* out;   // bf16 [T][H]
+  unsigned* ctr;   // counter block
+};
+constexpr int kFusedCtrBytes = 32768;
+constexpr int kFusedErrorWord = 0;  // ctr[0] != 0: a bounded wait gave up (never expected)
+hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s);
+
 // ------------------------------------------------------------------ combine
 // out[t] = bf16(sum_j w[t][j] * y_perm[inv_pos[t*K+j]] + y_shared[t]).
 hipError_t launch_combine(const void* y_perm, bool y_bf16, const int* inv_pos, const float* w,

@@ -60,6 +60,8 @@ struct TopkLayout {
 //   softmax over all experts; group score = max member; top-TG groups by
 //   rank (ties to the lower group); then K rounds of (largest logit among the
 //   kept groups' experts, ties to the lower id).  w = scale * softmax score.
+// COH: agent-scope atomic stores of ids / w (read by other workgroups in the same launch).
+template <bool COH = false>
 MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[kMpl], int* ids, float* w) {
   const int lane = lane_id();
   float mx = kNegInfF;
@@ -100,45 +102,52 @@ MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[
         if (j == bj) lg[j] = kNegInfF;
     }
     if (lane == 0) {
-      ids[r] = e;
-      w[r] = p.scale * (expf(v - m) / s);
+      const float wr = p.scale * (expf(v - m) / s);
+      if (COH) {
+        __hip_atomic_store(ids + r, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(w + r, wr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        ids[r] = e;
+        w[r] = wr;
+      }
     }
   }
 }
 
 // Router logits of one expert row e for T <= kRouteGemvMaxT tokens, computed
-// by one workgroup of 256 threads: all of the row's 16-byte loads are issued
-// before any arithmetic; partial sums meet in `part` (LDS) in wave order.
+// by one workgroup of 256 threads: all of the row's and the tokens' 16-byte
+// loads are issued before any arithmetic (rows past T reload row T-1 and are
+// masked, so no load sits behind a branch); partial sums meet in `part` (LDS)
+// in wave order.  coherent: agent-scope atomic stores of the logits (read by
+// another workgroup in the same launch).
 MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* __restrict__ wr, const RouteParams& p,
-                        int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT]) {
+                        int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT], bool coherent = false) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint16_t* row = wr + size_t(e) * p.H;
   float acc[kRouteGemvMaxT] = {};
   // 256 threads x 8 bf16 = 2048 columns per pass; 4 passes issued together
   for (int k0 = 0; k0 < p.H; k0 += 4 * 2048) {
-    u32x4 wv[4];
+    u32x4 wv[4], xv[4][kRouteGemvMaxT];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int k = min(k0 + c * 2048 + tid * 8, p.H - 8);
       wv[c] = *reinterpret_cast<const u32x4*>(row + k);
+#pragma unroll
+      for (int t = 0; t < kRouteGemvMaxT; ++t)
+        xv[c][t] = *reinterpret_cast<const u32x4*>(x + size_t(min(t, T - 1)) * p.H + k);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int kraw = k0 + c * 2048 + tid * 8;
-      const int k = min(kraw, p.H - 8);
-      const float on = kraw < p.H ? 1.0f : 0.0f;
+      const float on = k0 + c * 2048 + tid * 8 < p.H ? 1.0f : 0.0f;
 #pragma unroll
       for (int t = 0; t < kRouteGemvMaxT; ++t) {
-        if (t < T) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(x + size_t(t) * p.H + k);
-          float a = 0.f;
+        float a = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            a = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(wv[c][q] << 16), a);
-            a = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[c][q] & 0xffff0000u), a);
-          }
-          acc[t] = fmaf(a, on, acc[t]);
+        for (int q = 0; q < 4; ++q) {
+          a = fmaf(__uint_as_float(xv[c][t][q] << 16), __uint_as_float(wv[c][q] << 16), a);
+          a = fmaf(__uint_as_float(xv[c][t][q] & 0xffff0000u), __uint_as_float(wv[c][q] & 0xffff0000u), a);
         }
+        acc[t] = fmaf(a, on, acc[t]);
       }
     }
   }
@@ -148,7 +157,13 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
     if (lane == 0) part[wave][t] = v;
   }
   __syncthreads();
-  if (tid < T) logits[tid * p.E + e] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+  if (tid < T) {
+    const float v = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    if (coherent)
+      __hip_atomic_store(logits + tid * p.E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      logits[tid * p.E + e] = v;
+  }
 }
 
 // Load one token's logits (+ bias) into the layout.

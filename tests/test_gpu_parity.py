@@ -49,6 +49,14 @@ SMALL = {
     "bf16_1tok": small_cfg(0, tokens=1),
     "b128_4tok_noshared": small_cfg(1, tokens=4, hidden=256, n_experts=12, n_groups=3, topk_groups=2, topk=2,
                                     inter=128, shared_inter=0),
+    # small T with bf16 activations: the single-launch path
+    "mx_none_2tok": small_cfg(3, tokens=2, hidden=512, n_experts=8, inter=256, shared_inter=256,
+                              routed_afmt="none"),
+    "dsv2_like_4tok": small_cfg(1, tokens=4, hidden=1024, n_experts=64, n_groups=8, topk_groups=3, topk=6,
+                                inter=512, shared_inter=1024),
+    "mx_both_3tok": small_cfg(3, tokens=3, hidden=512, n_experts=8, inter=256, shared_inter=384,
+                              routed_afmt="none", shared_wfmt="mxfp8"),
+    "bf16_long_k_2tok": small_cfg(0, tokens=2, hidden=512, n_experts=16, topk=4, inter=1536, shared_inter=2048),
 }
 
 
@@ -242,12 +250,14 @@ def _forward(cfg, inp, x=None):
     return out, ids, w
 
 
-@pytest.mark.parametrize("path", ["auto", "gemv", "gemm"])
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm", "staged"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_small(name, path, monkeypatch):
     cfg = SMALL[name]
     if path == "gemm" and not pairs_ok(cfg):
         pytest.skip("no GEMM kernel for this format pair")
+    if path == "staged" and cfg.tokens > 4:
+        pytest.skip("the staged small-T path serves T <= 4")
     if path != "auto":
         monkeypatch.setenv("MOE_FORCE_PATH", path)
     inp = gpu_inputs(cfg)
@@ -299,6 +309,33 @@ def test_forward_zero_tokens_is_noop():
     layer.forward(inp.x[:0], out=out, ids=torch.empty(0, cfg.topk, dtype=torch.int32, device=DEV),
                   w=torch.empty(0, cfg.topk, dtype=torch.float32, device=DEV))
     torch.cuda.synchronize()
+
+
+def _queue_words(layer):
+    return layer.ws[:32768].view(torch.int32).cpu().numpy()
+
+
+def test_single_launch_queue_across_calls():
+    """The single-launch small-T path over many calls on one workspace, with
+    T changing between 1 and 4 and two layers interleaved on one stream:
+    every output matches the oracle and the queue state is zero after each
+    call (no bounded wait gave up, every counter reset)."""
+    layers = []
+    for name in ("dsv2_like_4tok", "bf16_1tok"):
+        cfg = SMALL[name].derive(tokens=4)
+        inp = gpu_inputs(cfg)
+        r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+        layers.append((name, moe.Layer(cfg, inp), inp, r))
+    for it in range(12):
+        for name, layer, inp, r in layers:
+            T = 1 + (it * 3 + len(name)) % 4
+            say(f"[single-launch] {name} call {it} T={T}")
+            out, ids, w = layer.forward(inp.x[:T].contiguous())
+            torch.cuda.synchronize()
+            assert np.array_equal(ids.cpu().numpy(), r.ids[:T])
+            assert np.max(np.abs(w.cpu().numpy() - r.w[:T]) / r.w[:T]) <= WTOL
+            assert rel_err(oracle.bf16_to_f64(out), r.out[:T]) <= TOL
+            assert not _queue_words(layer).any()
 
 
 def test_forward_reuses_workspace_across_sizes():
