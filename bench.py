@@ -145,12 +145,16 @@ def main():
     gbps = bytes_step / (us * 1e-6) / 1e9
 
     kern = trace_kernels(layers, xs, min(args.steps, 100), moe, torch)
-    if "decode_fused" in kern:  # the whole layer in one launch: its bytes are the step's
-        dom, dom_bytes = "decode_fused", bytes_step
+    if list(kern) == ["decode_fused"]:
+        # the whole layer is one launch: its bytes are the step's, and the
+        # timed loop (back-to-back launches, events around the loop on the
+        # launch stream) gives its average duration without per-launch events
+        dom, dom_bytes, dom_us = "decode_fused", bytes_step, us
     else:  # staged launches: the routed gate/up is the largest single stream (94 MB)
         dom, dom_bytes = "gemv_gate_up", statistics.mean(gu_bytes)
-    dom_us = kern[dom][0] * 1e3
+        dom_us = kern[dom][0] * 1e3
     dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(dom)
 
     out = {
         "metric": METRIC,
@@ -184,7 +188,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": int(dom_bytes),
             "launch_us": round(dom_us, 3),
         },
@@ -197,6 +201,33 @@ def main():
         out["cpu_baseline"] = cpu_baseline(cfg, reps[0], layers[0], torch)
 
     print(json.dumps(out), flush=True)
+
+
+def csrc_hash():
+    import hashlib
+    csrc = os.path.join(ROOT, "mixture_experts_layer_router_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary of `kernel`, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_dsv2_b1_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("csrc sha256 at measurement") != csrc_hash() or "traffic_bytes" not in fields:
+        return None
+    return int(fields["traffic_bytes"])
 
 
 def secondary(args, moe, synth, torch):
@@ -230,17 +261,18 @@ def cpu_baseline(cfg, inp, lay, torch):
     routed = HostExperts(inp.routed, touched)
     shared = HostExperts(inp.shared, [0])
     x, wr = inp.x.cpu(), inp.w_router.cpu()
+    cores = len(os.sched_getaffinity(0))
     times = []
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         deadline = time.perf_counter() + 20.0
         while len(times) < 3 and (not times or time.perf_counter() < deadline):
             t0 = time.perf_counter()
             oracle.forward(cfg, x, wr, None, routed, shared)
             times.append(time.perf_counter() - t0)
     s = statistics.median(times)
-    return {"value": round(s * 1e6, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"the B=1 layer forward (replica 0), median of {len(times)} runs, "
-                      "float64 numpy with BLAS limited to one thread"}
+    return {"value": round(s * 1e6, 1), "unit": "us/layer", "cores": cores, "kind": "oracle",
+            "sample": f"the whole B=1 layer forward (replica 0: router, top-k, the 6 routed and the shared "
+                      f"expert, combine), median of {len(times)} runs, float64 numpy with BLAS on {cores} threads"}
 
 
 if __name__ == "__main__":
