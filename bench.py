@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 2048-token workload")
     ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--secondary-only", action="store_true",
+                    help="only run the 2048-token workload (for profiling its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -121,6 +123,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 5}))
+        return
+    if args.secondary_only:
+        print(json.dumps({"secondary": secondary(args, moe, synth, torch)}), flush=True)
         return
     cfg = synth.get_config("dsv2_b1")
     reps = [synth.make_inputs(cfg, dev, replica=r) for r in range(args.replicas)]

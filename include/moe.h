@@ -40,7 +40,8 @@
  *                       16, route_scale not finite, bad format code
  *     MOE_EALIGN        a pointer not 16-byte aligned, or hidden, inter or
  *                       shared_inter not a multiple of 128
- *     MOE_EUNSUPPORTED  n_experts > 256, n_groups > 64, or a weight /
+ *     MOE_EUNSUPPORTED  n_experts > 256, n_groups > 64, an FP8_B128 format
+ *                       with hidden, inter or shared_inter above 8192, or a weight /
  *                       activation format pair that no kernel implements
  *     MOE_EWORKSPACE    ws_bytes below moe_workspace_size()
  *     MOE_EHIP          a HIP launch failed

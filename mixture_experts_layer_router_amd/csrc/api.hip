@@ -57,6 +57,10 @@ moe_status check_cfg(const moe_config* c) {
   if (c->n_experts > 256 || c->n_groups > 64) return MOE_EUNSUPPORTED;
   if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128) return MOE_EALIGN;
   if (!any_pair(c->routed_wfmt, c->routed_afmt)) return MOE_EUNSUPPORTED;
+  // the FP8_B128 GEMM stages all K steps' weight scales in LDS
+  for (int f : {c->routed_wfmt, c->shared_wfmt})
+    if (f == W_FP8_B128 && (c->hidden > kGemmMaxK || c->inter > kGemmMaxK || c->shared_inter > kGemmMaxK))
+      return MOE_EUNSUPPORTED;
   if (c->shared_inter > 0 && !any_pair(c->shared_wfmt, c->shared_afmt)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -107,7 +111,7 @@ Ws plan(const moe_config* c, int Tm) {
     return at;
   };
   s.counter = take(kFusedCtrBytes);  // must stay at offset 0 (documented in moe.h)
-  s.logits = take(T * E * 4);
+  s.logits = take(T * E * 4 * (T > size_t(kRouteGemvMaxT) ? kRouterMaxSplit : 1));  // split-K slices
   s.ids = take(TK * 4);
   s.w = take(TK * 4);
   s.offsets = take((E + 1) * 4);
@@ -186,8 +190,13 @@ moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_
   g.M = T;
   g.C = at<float>(ws, L.logits);
   g.ldc = c->n_experts;
+  // N = E is at most one tile wide: split K so the launch fills the chip; the
+  // top-k adds the slices in a fixed order
+  const int mt = (T + kGemmBM - 1) / kGemmBM, steps = c->hidden * 2 / 128;
+  g.ksplit = std::max(1, std::min({kRouterMaxSplit, 256 / mt, steps}));
+  g.c_split = long(T) * c->n_experts;
   LAUNCH("gemm_router_logits", launch_gemm(W_BF16, EPI_F32, g, s));
-  LAUNCH("topk", launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s));
+  LAUNCH("topk", launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s, g.ksplit, g.c_split));
   return MOE_OK;
 }
 

@@ -18,9 +18,12 @@ struct RouteParams {
 constexpr int kRouteGemvMaxT = 4;
 hipError_t launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const RouteParams& p,
                                float* logits, hipStream_t s);
-// Top-k over precomputed fp32 logits [T][E] (bias added here).
+// Top-k over precomputed fp32 logits [T][E] (bias added here).  The logits
+// may come as nslice partial sums at stride slice_stride (elements), added in
+// slice order.
 hipError_t launch_topk(const float* logits, int T, const float* bias, const RouteParams& p, int* ids,
-                       float* w, hipStream_t s);
+                       float* w, hipStream_t s, int nslice = 1, long slice_stride = 0);
+constexpr int kRouterMaxSplit = 16;  // K slices of the batched router GEMM
 
 // ------------------------------------------------------------------ dispatch
 // ids [TK]; writes offsets [E+1], perm_src [TK], inv_pos [TK]; when tiles is
@@ -74,8 +77,13 @@ struct GemmParams {
   void* Cs;       // scales of quantised h (EPI_GATEUP with out_afmt != A_NONE)
   int out_afmt;   // EPI_GATEUP: A_NONE -> bf16 h; else quantised h
   float* C_f32;   // EPI_GATEUP only: if non-null, h is written as fp32 here instead
+  // EPI_F32 only: the K steps are split into ksplit slices (0 or 1: none); slice
+  // z writes its partial product to C + z * c_split (elements)
+  int ksplit;
+  long c_split;
 };
-constexpr int kGemmBM = 64;
+constexpr int kGemmBM = 128;
+constexpr int kGemmMaxK = 8192;  // FP8_B128 GEMM: K (elements) <= this
 hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ small-batch GEMV FFN

@@ -27,12 +27,12 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
 // One wave per token over fp32 logits [T][E] (bias added here).
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T,
                                                    const float* __restrict__ bias, RouteParams p, int* ids,
-                                                   float* w) {
+                                                   float* w, int nslice, long slice_stride) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave
   const TopkLayout L(p, lane_id());
   float lg[kMpl];
-  topk_load(p, L, logits + size_t(t) * p.E, bias, lg);
+  topk_load(p, L, logits + size_t(t) * p.E, bias, lg, nslice, slice_stride);
   topk_select(p, L, lg, ids + size_t(t) * p.K, w + size_t(t) * p.K);
 }
 
@@ -45,8 +45,9 @@ hipError_t launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, con
 }
 
 hipError_t launch_topk(const float* logits, int T, const float* bias, const RouteParams& p, int* ids, float* w,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, bias, p, ids, w);
+                       hipStream_t s, int nslice, long slice_stride) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, bias, p, ids, w,
+                     nslice < 1 ? 1 : nslice, slice_stride);
   return hipGetLastError();
 }
 

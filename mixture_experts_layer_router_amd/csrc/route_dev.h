@@ -166,15 +166,17 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
   }
 }
 
-// Load one token's logits (+ bias) into the layout.
+// Load one token's logits (+ bias) into the layout.  The logits may be the sum
+// of nslice partial slices (stride slice_stride elements), added in order.
 MOE_DEV void topk_load(const RouteParams& p, const TopkLayout& L, const float* logits_row, const float* bias,
-                       float (&lg)[kMpl]) {
+                       float (&lg)[kMpl], int nslice = 1, long slice_stride = 0) {
 #pragma unroll
   for (int j = 0; j < kMpl; ++j) {
     const int e = L.expert(p, j);
     float v = kNegInfF;
     if (e >= 0) {
       v = logits_row[e];
+      for (int z = 1; z < nslice; ++z) v += logits_row[z * slice_stride + e];
       if (bias) v += bias[e];
     }
     lg[j] = v;
