@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--secondary-only", action="store_true",
                     help="only run the 2048-token workload (for profiling its kernels)")
+    ap.add_argument("--sources-hash", metavar="KERNEL", help="print the sources hash recorded with KERNEL's counters")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -105,6 +106,9 @@ def trace_kernels(layers, xs, steps, moe, torch):
 
 def main():
     args = parse()
+    if args.sources_hash:
+        print(csrc_hash(args.sources_hash))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -208,11 +212,18 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def csrc_hash():
+# sources each measured kernel is built from: its counter summary stays valid
+# while these files are unchanged
+KERNEL_SOURCES = {
+    "decode_fused": ("decode.hip", "gemv_dev.h", "route_dev.h", "common.h", "kernels.h"),
+}
+
+
+def csrc_hash(kernel):
     import hashlib
     csrc = os.path.join(ROOT, "mixture_experts_layer_router_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES.get(kernel, sorted(os.listdir(csrc))):
         h.update(f.encode())
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
@@ -230,7 +241,7 @@ def measured_traffic(kernel):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("csrc sha256 at measurement") != csrc_hash() or "traffic_bytes" not in fields:
+    if fields.get("sources sha256 at measurement") != csrc_hash(kernel) or "traffic_bytes" not in fields:
         return None
     return int(fields["traffic_bytes"])
 

@@ -192,6 +192,7 @@ moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_
   g.ldc = c->n_experts;
   // N = E is at most one tile wide: split K so the launch fills the chip; the
   // top-k adds the slices in a fixed order
+  // (N = E is small: the launcher keeps this on the 128-row kernel, 128-byte K steps)
   const int mt = (T + kGemmBM - 1) / kGemmBM, steps = c->hidden * 2 / 128;
   g.ksplit = std::max(1, std::min({kRouterMaxSplit, 256 / mt, steps}));
   g.c_split = long(T) * c->n_experts;
@@ -204,7 +205,7 @@ moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_
 // shared expert).  A: activation rows in `afmt` (bf16 when A_NONE); a_map
 // gathers rows.  Output: y (fp32 or bf16) [rows][H].
 moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void* As, const int* a_map, int a_div,
-                    int rows, const int* seg, const int* tiles, const int* ntiles, int maxt,
+                    int rows, const int* seg, const int* tiles, const int* ntiles, int maxt, int bm,
                     const moe_ffn_weights* W, void* h, void* hs, void* y, bool y_bf16, hipStream_t s) {
   const int wf = routed ? c->routed_wfmt : c->shared_wfmt;
   const int af = routed ? c->routed_afmt : c->shared_afmt;
@@ -230,6 +231,7 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   g.tiles = tiles;
   g.ntiles = ntiles;
   g.max_tiles = maxt;
+  g.bm = bm;
   g.C = h;
   g.ldc = I;
   g.Cs = hs;
@@ -250,6 +252,7 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   d.tiles = tiles;
   d.ntiles = ntiles;
   d.max_tiles = maxt;
+  d.bm = bm;
   d.C = y;
   d.ldc = H;
   LAUNCH(routed ? "gemm_down_routed" : "gemm_down_shared", launch_gemm(wf, y_bf16 ? EPI_BF16 : EPI_F32, d, s));
@@ -409,13 +412,14 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t which, const void* x, c
   int* tiles = nullptr;
   int* ntiles = nullptr;
   int maxt = 0;
+  const int bm = ffn_tile_rows(wf, H, I);
   if (routed) {
     tiles = at<int>(ws, L.tiles);
     ntiles = at<int>(ws, L.ntiles);
-    maxt = max_tiles(rows, E, kGemmBM);
-    LAUNCH("build_tiles", launch_build_tiles(seg_offsets, E, rows, kGemmBM, tiles, ntiles, stream));
+    maxt = max_tiles(rows, E, bm);
+    LAUNCH("build_tiles", launch_build_tiles(seg_offsets, E, rows, bm, tiles, ntiles, stream));
   }
-  return gemm_ffn(cfg, routed, A, As, nullptr, 1, rows, routed ? seg_offsets : nullptr, tiles, ntiles, maxt, W,
+  return gemm_ffn(cfg, routed, A, As, nullptr, 1, rows, routed ? seg_offsets : nullptr, tiles, ntiles, maxt, bm, W,
                   at<void>(ws, routed ? L.h : L.hsh), at<void>(ws, routed ? L.hs : L.hshs), y, false, stream);
 }
 
@@ -644,7 +648,8 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   int* inv = at<int>(ws, L.inv);
   int* tiles = at<int>(ws, L.tiles);
   int* ntiles = at<int>(ws, L.ntiles);
-  LAUNCH("permute", launch_permute(ids, TK, E, off, perm, inv, tiles, ntiles, kGemmBM, stream));
+  const int rbm = ffn_tile_rows(cfg->routed_wfmt, H, cfg->inter);
+  LAUNCH("permute", launch_permute(ids, TK, E, off, perm, inv, tiles, ntiles, rbm, stream));
   const void* xa = x;
   const void* xas = nullptr;
   if (raf != A_NONE) {
@@ -653,7 +658,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
     xa = at<void>(ws, L.xq);
     xas = at<void>(ws, L.xqs);
   }
-  if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, kGemmBM), routed,
+  if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, rbm), rbm, routed,
                      at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
     return st;
   float* ysh = nullptr;
@@ -672,7 +677,8 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
       }
     }
     ysh = at<float>(ws, L.ysh);
-    if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0, shared, at<void>(ws, L.hsh),
+    if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
+                       ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
                        at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
       return st;
   }

@@ -57,6 +57,18 @@ MOE_DEV uint32_t f32_to_e4m3(float v) {
   return code | sign;
 }
 
+// Four fp32 -> four e4m3fn codes (byte k from the k-th argument) with the
+// hardware converter: round to nearest even; the inputs are clamped to
+// +-448 first, which gives the saturation of f32_to_e4m3 (the converter
+// alone turns overflow into NaN).  Equal to f32_to_e4m3 for every non-NaN
+// input (checked on all fp32 magnitudes below 1024 on gfx950).
+MOE_DEV uint32_t e4m3x4_sat(float a, float b, float c, float d) {
+  auto cl = [](float v) { return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return uint32_t(w);
+}
+
 // ---------------------------------------------------------------- e8m0
 MOE_DEV float e8m0_to_f32(uint32_t c) { return __builtin_amdgcn_ldexpf(1.0f, int(c) - 127); }
 

@@ -3,380 +3,454 @@
 //
 //   C[r][n] = sum_k A[r][k] * B_e[n][k]   for the rows r of expert e's segment
 //
-// Weight formats and the matrix-core instruction each uses:
-//   bf16      v_mfma_f32_16x16x32_bf16, two per 128-byte K step
-//   FP8_B128  v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales; one
-//             instruction covers exactly one 128-deep K block, and its fp32
-//             result is promoted into the accumulator with the block's
-//             activation scale (per row) times weight scale (per 128 rows)
-//   MXFP8     v_mfma_scale_f32_16x16x128_f8f6f4 with the e8m0 scales of A and
-//             B passed per lane (lane l scales row l%16, K block l/16)
+// Weight formats and the matrix-core instruction each uses (32x32 output
+// blocks: on gfx950 these issue at 4.4 PFLOP/s FP8 and 2.2 PFLOP/s bf16 from
+// one wave per SIMD, against 3.5 and 1.25 for the 16x16 shapes):
+//   bf16      v_mfma_f32_32x32x16_bf16, four per 128-byte K step
+//   MXFP8     v_mfma_scale_f32_32x32x64_f8f6f4, two per step, with the e8m0
+//             scales of A and B passed per lane (lane l scales row l%32 of its
+//             operand for the 32-deep K block l/32 of the instruction)
+//   FP8_B128  the same instruction with unit scales; the two of one 128-deep
+//             K block accumulate into a temporary, which is promoted into the
+//             accumulator with the block's activation scale (per row) times
+//             its weight scale (per 128 B rows)
 //
-// Tile: 128 rows x 256 B-rows x 128 bytes of K per step; 4 waves, each owning
-// 64 rows x 128 B-rows (4 x 8 MFMA tiles of 16x16), so every operand read from
-// LDS feeds 4 or 8 MFMAs.  Tiles move HBM -> LDS with direct-to-LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), three
-// stages deep, so two steps of loads are in flight during the MFMAs of a
-// third.  Each lane fetches the global chunk that belongs at its LDS slot, so
-// the LDS image is swizzled (chunk c of row r sits at c ^ ((r >> 1) & 7)):
-// the 16 lanes that read one operand column hit 16 distinct bank groups.
-// Activation and MX weight scales travel the same way, one dword per row.
+// Tile: 128 rows x 256 B rows x 128 bytes of K per step; 4 waves, each owning
+// 64 rows x 128 B rows (2 x 4 blocks of 32x32).  Tiles move HBM -> LDS with
+// direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
+// base + 16 l), three stages deep.  The LDS image is swizzled (16-byte chunk c
+// of row r sits at c ^ ((r >> 1) & 7)) so that the 16 lanes of one LDS read
+// cycle hit 16 distinct bank groups.  Operand layout in registers: for slot
+// c = 0..3 of a 128-byte step, lane l reads chunk 2c + l/32 of row l%32 of its
+// block; an FP8 instruction for K half h takes slots 2h and 2h+1 (K bytes
+// [16g, 16g+16) and [32+16g, 48+16g) of the half, g = l/32), a bf16
+// instruction for K quarter q takes slot q.
+//
+// bf16 and MXFP8 keep two register sets of operands: the reads of step s+1
+// are issued among the MFMAs of step s, together with the direct-to-LDS loads
+// of step s+3, in a fixed interleave, so the matrix pipe does not wait for LDS
+// at the step boundary.  FP8_B128 needs the registers for its temporaries and
+// reads each step's operands at the start of the step.
 //
 // Rows come from a device tile list written by the dispatch kernel, so no
-// expert count is read back to the host (Mixture-of-Kittens, Abstract).  The
-// flat list of (expert, n-block, m-tile) tiles is cut into 8 contiguous
-// ranges, one per XCD (blocks are dispatched round robin over the XCDs): the
-// tiles that run together on one XCD share their weight panel (m-tiles of the
-// same n-block are adjacent) and their activation panel (same expert), so the
-// XCD's L2 serves the repeats.
+// expert count is read back to the host (Mixture-of-Kittens, Abstract); the
+// tile order is gemm_dev.h's XCD-aware schedule.  In the FP8_B128 path a wave
+// whose second 32-row block lies past the tile's valid rows skips that
+// block's MFMAs.  This kernel serves FP8_B128, MXFP8 with K not a multiple of
+// 512, and the dense GEMMs too small to fill the chip with 256-row tiles
+// (gemm2.hip serves the rest).
 //
 // EPI_GATEUP: B-tile rows [128w, 128w+64) are gate rows and [128w+64, 128w+128)
-// the up rows of the same 64 intermediate columns, so every lane owns g and u
-// of the same (row, column) and the epilogue writes h = SiLU(g) * u directly,
-// optionally quantised to e4m3 per 1x128 or 1x32 block ("From 35 to 873
-// tokens/s", Rounds 12-15: the next matmul's input quantised by the producer).
-#include "common.h"
-#include "kernels.h"
+// the up rows of the same 64 intermediate columns, so blocks j and j+2 of a
+// wave hold g and u of the same (row, column) and the epilogue writes
+// h = SiLU(g) * u directly, optionally quantised to e4m3 per 1x128 or 1x32
+// block ("From 35 to 873 tokens/s", Rounds 12-15: the next matmul's input
+// quantised by the producer).
+#include "gemm_dev.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;   // 128 rows
-constexpr int BNT = 256;      // B rows per tile
-constexpr int BKB = 128;      // bytes of K per step
+using namespace gemm_dev;
+
+constexpr int BM = kGemmBM;  // 128 rows
+constexpr int BNT = 256;     // B rows per tile
+constexpr int BKB = 128;     // bytes of K per step
 constexpr int kStages = 3;
-constexpr int kLdsA = BM * BKB;    // 16 KB
-constexpr int kLdsB = BNT * BKB;   // 32 KB
-constexpr int kLdsAS = BM * 4;     // one scale dword per A row per step
-constexpr int kLdsBS = BNT * 4;    // one scale dword per B row per step (MX)
-constexpr int kMaxKSteps = 64;     // FP8_B128: K <= 8192 (checked by the host)
-
-template <int WF>
-MOE_DEV constexpr int esz() { return WF == W_BF16 ? 2 : 1; }
-
-// LDS byte offset of 16-byte chunk c of tile row r
-MOE_DEV int swz(int r, int c) { return r * BKB + ((c ^ ((r >> 1) & 7)) << 4); }
-
-// Direct-to-LDS loads: the 64 lanes' data lands at lds_base + 16 l (x4) or
-// + 4 l (x1).  lds_base is wave-uniform.  M0 is reserved for this use; nothing
-// else in these kernels reads it.
-MOE_DEV void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory");
-}
-MOE_DEV void dma4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory");
-}
-template <int N>
-MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-MOE_DEV void barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-MOE_DEV uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(p)));
-}
+constexpr int kLdsA = BM * BKB;   // 16 KB
+constexpr int kLdsB = BNT * BKB;  // 32 KB
+constexpr int kMaxKSteps = kGemmMaxK / 128;
 
 template <int WF>
 MOE_DEV constexpr int scale_dmas() { return WF == W_MXFP8 ? 2 : (WF == W_FP8_B128 ? 1 : 0); }
 template <int WF>
 MOE_DEV constexpr int dmas_per_stage() { return 4 + 8 + scale_dmas<WF>(); }
 
+
+// one step's operands of one lane: slot c of block i sits in half c%2 of
+// a[i][c/2], so an FP8 instruction for K half h takes a[i][h] whole
+struct Frag {
+  i32x8 a[2][2];  // [32-row block i][K half]
+  i32x8 b[4][2];  // [32-row B block j][K half]
+  uint32_t sa[2], sb[4];  // MXFP8: the four e8m0 scales of the step, one byte per K block
+};
+MOE_DEV void set_slot(i32x8& v, int c, i32x4 x) {
+  if (c & 1)
+    v.hi = x;
+  else
+    v.lo = x;
+}
+MOE_DEV i32x4 get_slot(const i32x8& v, int c) { return (c & 1) ? v.hi : v.lo; }
+
 template <int WF, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[kStages][kLdsA];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[kStages][kLdsB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * (kLdsA + kLdsB)];
   __shared__ __attribute__((aligned(16))) uint32_t sAS[kStages][BM];
   __shared__ __attribute__((aligned(16))) uint32_t sBS[WF == W_MXFP8 ? kStages : 1][WF == W_MXFP8 ? BNT : 1];
   __shared__ float sAmax[2][BM];
   __shared__ float sWs[WF == W_FP8_B128 ? 4 : 1][2][WF == W_FP8_B128 ? kMaxKSteps : 1];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 5, l32 = lane & 31;
   const int nper = EPI == EPI_GATEUP ? BNT / 2 : BNT;  // output columns per tile
-  const int NB = (p.N + nper - 1) / nper;
-
-  // ---------------------------------------------------------- tile schedule
-  const int nt_list = p.tiles ? p.ntiles[0] : (p.M + BM - 1) / BM;
   const int KS = (EPI == EPI_F32 && p.ksplit > 1) ? p.ksplit : 1;
-  const int T = nt_list * NB * KS;
-  const int chunk = (T + 7) / 8;
-  int idx = int(blockIdx.x % 8) * chunk + int(blockIdx.x / 8);
-  if (int(blockIdx.x / 8) >= chunk || idx >= T) return;
-  const int kz = idx % KS;  // K slice (split-K: slices of one tile are adjacent)
-  idx /= KS;
-  int e = 0, m0, nb;
-  {
-    const int pe = idx / NB;  // a tile-list entry of the same expert
-    int be = 0, ne = nt_list;
-    if (p.tiles) {
-      e = p.tiles[2 * pe];
-      be = pe - p.tiles[2 * pe + 1] / BM;
-      const int c0 = min(max(p.seg[e], 0), p.M), c1 = min(max(p.seg[e + 1], c0), p.M);
-      ne = max((c1 - c0 + BM - 1) / BM, 1);
-    }
-    const int local = idx - be * NB;
-    nb = local / ne;
-    m0 = (local % ne) * BM;
-  }
-  // segment bounds clamped to [0, M] so malformed offsets cannot address outside the rows
-  const int seg0 = p.seg ? min(max(p.seg[e], 0), p.M) : 0;
-  const int seg1 = p.seg ? min(max(p.seg[e + 1], seg0), p.M) : p.M;
-  const int mrows = min(BM, seg1 - seg0 - m0);
-  if (mrows <= 0) return;
-  const int n0 = nb * nper;
+  const Tile tl = tile_of(p, BM, nper, KS);
+  if (!tl.valid) return;
+  const int e = tl.e, m0 = tl.m0, n0 = tl.n0, seg0 = tl.seg0, mrows = tl.mrows, kz = tl.kz;
   const int K = p.K;
+  const int N = p.N;
   const int nk_all = K * esz<WF>() / BKB;
   const int ks0 = int(long(nk_all) * kz / KS), ks1 = int(long(nk_all) * (kz + 1) / KS);
   const int nk = ks1 - ks0;  // K steps of this slice, starting at step ks0
-  const size_t lda_b = size_t(p.lda) * esz<WF>();
-  const size_t ldb_b = size_t(K) * esz<WF>();
-  const uint8_t* b0 = static_cast<const uint8_t*>(p.B0) + size_t(e) * p.b_stride * esz<WF>();
-  const uint8_t* b1 = p.B1 ? static_cast<const uint8_t*>(p.B1) + size_t(e) * p.b_stride * esz<WF>() : nullptr;
+  const uint32_t lda_b = uint32_t(p.lda) * esz<WF>();
+  const uint32_t ldb_b = uint32_t(K) * esz<WF>();
 
   const int* a_map = p.a_map;
   const int a_div = p.a_div;
   const int rbase = seg0 + m0, rlast = mrows - 1;
-  const int N = p.N;
   // global row of tile row rl (clamped into the segment)
-#define PHYS_ROW(rl) (a_map ? a_map[rbase + min((rl), rlast)] / a_div : rbase + min((rl), rlast))
+#define PHYS_ROW(rl) uint32_t(a_map ? a_map[rbase + min((rl), rlast)] / a_div : rbase + min((rl), rlast))
 
   // ---------------------------------------------------------- DMA sources
   // A: wave w loads tile rows [32w, 32w+32) as 4 blocks of 8 rows; lane L
   // fetches row 8i + L/8 of its block, chunk (L%8) ^ ((row>>1)&7).
-  const uint8_t* ga[4];
+  const uint8_t* a_base = uniform_ptr(p.A);
+  uint32_t oa[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 32 * wave + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    ga[i] = static_cast<const uint8_t*>(p.A) + size_t(PHYS_ROW(r)) * lda_b + c * 16;
+    oa[i] = PHYS_ROW(r) * lda_b + c * 16;
   }
-  const uint8_t* gb[8];
+  // B: wave w loads tile B rows [64w, 64w+64); for EPI_GATEUP these are gate
+  // rows (w even) or up rows (w odd) of intermediate columns n0 + 64 (w/2) + [0, 64)
+  const uint8_t* b_base;
+  uint32_t ob[8];
+  {
+    const void* bsrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1 : p.B0;
+    b_base = uniform_ptr(static_cast<const uint8_t*>(bsrc) + size_t(e) * p.b_stride * esz<WF>());
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = 64 * wave + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ ((t >> 1) & 7);
-    const uint8_t* base = b0;
-    int br;
-    if (EPI == EPI_GATEUP) {
-      const int w = t >> 7, u = t & 127;
-      base = u < 64 ? b0 : b1;
-      br = n0 + 64 * w + (u & 63);
-    } else {
-      br = min(n0 + t, N - 1);
+    for (int i = 0; i < 8; ++i) {
+      const int t = 64 * wave + 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((t >> 1) & 7);
+      const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + 8 * i + (lane >> 3) : min(n0 + t, N - 1);
+      ob[i] = uint32_t(br) * ldb_b + c * 16;
     }
-    gb[i] = base + size_t(br) * ldb_b + c * 16;
   }
   // scales: A rows (waves 0,1 own rows [64w, 64w+64); waves 2,3 repeat them, so
   // every wave issues the same number of loads), MX weight rows (64 per wave)
-  const int kb_a = WF == W_MXFP8 ? K / 32 : K / 128;  // scale units per A row
-  const uint8_t* gas = nullptr;
-  const uint8_t* gbs = nullptr;
-  if (WF != W_BF16) {
-    const int r = 64 * (wave & 1) + lane;
-    gas = static_cast<const uint8_t*>(p.As) + size_t(PHYS_ROW(r)) * (WF == W_MXFP8 ? kb_a : kb_a * 4);
+  const uint8_t* as_base = nullptr;
+  const uint8_t* bs_base = nullptr;
+  uint32_t oas = 0, obs = 0;
+  if constexpr (WF != W_BF16) {
+    as_base = uniform_ptr(p.As);
+    const int r = 64 * wm + lane;
+    oas = PHYS_ROW(r) * (WF == W_MXFP8 ? uint32_t(K / 32) : uint32_t(K / 128) * 4u);
   }
-  if (WF == W_MXFP8) {
-    const int t = 64 * wave + lane;
-    int br;
-    const uint8_t* base;
-    if (EPI == EPI_GATEUP) {
-      const int w = t >> 7, u = t & 127;
-      base = static_cast<const uint8_t*>(u < 64 ? p.B0s : p.B1s);
-      br = n0 + 64 * w + (u & 63);
-    } else {
-      base = static_cast<const uint8_t*>(p.B0s);
-      br = min(n0 + t, p.N - 1);
-    }
-    gbs = base + size_t(e) * p.bs_stride + size_t(br) * (K / 32);
+  if constexpr (WF == W_MXFP8) {
+    const void* ssrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1s : p.B0s;
+    bs_base = uniform_ptr(static_cast<const uint8_t*>(ssrc) + size_t(e) * p.bs_stride);
+    const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + lane : min(n0 + 64 * wave + lane, N - 1);
+    obs = uint32_t(br) * uint32_t(K / 32);
   }
+#undef PHYS_ROW
   // FP8_B128 weight scales: one per (128 B rows, 128 K); a wave's B rows sit in
   // one gate block and one up block (GATEUP) or one block.  All K steps' scales
   // go to LDS before the main loop, which then issues no global load of its own.
   if constexpr (WF == W_FP8_B128) {
     const int kb = K / 128;
     for (int q = tid; q < 4 * 2 * kb; q += 256) {
-      const int w = q / (2 * kb), g = (q / kb) & 1, ks = q % kb;
+      const int w = q / (2 * kb), gg = (q / kb) & 1, ks = q % kb;
       const int wnq = w >> 1;
       const float* src;
       if (EPI == EPI_GATEUP)
-        src = static_cast<const float*>(g ? p.B1s : p.B0s) + size_t(e) * p.bs_stride + size_t(n0 / 128) * kb;
+        src = static_cast<const float*>(gg ? p.B1s : p.B0s) + size_t(e) * p.bs_stride + size_t(n0 / 128) * kb;
       else
         src = static_cast<const float*>(p.B0s) + size_t(e) * p.bs_stride +
-              size_t(min((n0 + 128 * wnq) / 128, p.N / 128 - 1)) * kb;
-      sWs[w][g][ks] = src[ks];
+              size_t(min((n0 + 128 * wnq) / 128, N / 128 - 1)) * kb;
+      sWs[w][gg][ks] = src[ks];
     }
     __syncthreads();
   }
 
-#undef PHYS_ROW
+  const uint32_t lds_a0 = lds_addr(smem), lds_b0 = lds_a0 + kStages * kLdsA;
+  // direct-to-LDS load d of K step kstep into stage st
+  auto dma_op = [&](int d, int st, int kstep) {
+    if (d < 4) {
+      dma16(oa[d], a_base + size_t(kstep) * BKB, lds_a0 + st * kLdsA + (32 * wave + 8 * d) * BKB);
+    } else if (d < 12) {
+      dma16(ob[d - 4], b_base + size_t(kstep) * BKB, lds_b0 + st * kLdsB + (64 * wave + 8 * (d - 4)) * BKB);
+    } else if (d == 12) {
+      dma4(oas, as_base + 4 * kstep, lds_addr(&sAS[st][64 * wm]));
+    } else if constexpr (WF == W_MXFP8) {
+      dma4(obs, bs_base + 4 * kstep, lds_addr(&sBS[st][64 * wave]));
+    }
+  };
+  constexpr int DPS = dmas_per_stage<WF>();
   auto issue = [&](int s) {
-    const int st = s % kStages;
-    const size_t ko = size_t(s + ks0) * BKB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(ga[i] + ko, lds_addr(&sA[st][(32 * wave + 8 * i) * BKB]));
+    for (int d = 0; d < DPS; ++d) dma_op(d, s % kStages, s + ks0);
+  };
+
+  // LDS operand reads: lane's row within its block is l32; slot c reads chunk 2c + g
+  int colo[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(gb[i] + ko, lds_addr(&sB[st][(64 * wave + 8 * i) * BKB]));
-    if constexpr (WF == W_MXFP8) {
-      dma4(gas + 4 * (s + ks0), lds_addr(&sAS[st][64 * (wave & 1)]));
-      dma4(gbs + 4 * (s + ks0), lds_addr(&sBS[st][64 * wave]));
-    } else if constexpr (WF == W_FP8_B128) {
-      dma4(gas + 4 * (s + ks0), lds_addr(&sAS[st][64 * (wave & 1)]));
+  for (int c = 0; c < 4; ++c) colo[c] = ((2 * c + g) ^ ((l32 >> 1) & 7)) << 4;
+  const int rowA = (64 * wm + l32) * BKB, rowB = (128 * wn + l32) * BKB;
+  // read r of a step: A slots (i, c) for i < NI, then B slots (j, c), then MX scales
+  auto read_op = [&](int r, Frag& f, int st, auto ni_t) {
+    constexpr int NI = decltype(ni_t)::value;
+    const uint8_t* As_ = smem + st * kLdsA;
+    const uint8_t* Bs_ = smem + kStages * kLdsA + st * kLdsB;
+    if (r < NI * 4) {
+      const int i = r / 4, c = r % 4;
+      set_slot(f.a[i][c >> 1], c, *reinterpret_cast<const i32x4*>(As_ + rowA + 32 * BKB * i + colo[c]));
+    } else if (r < NI * 4 + 16) {
+      const int j = (r - NI * 4) / 4, c = (r - NI * 4) % 4;
+      set_slot(f.b[j][c >> 1], c, *reinterpret_cast<const i32x4*>(Bs_ + rowB + 32 * BKB * j + colo[c]));
+    } else if (r < NI * 5 + 16) {
+      const int i = r - NI * 4 - 16;
+      f.sa[i] = sAS[st][64 * wm + 32 * i + l32];
+    } else {
+      const int j = r - NI * 5 - 16;
+      f.sb[j] = sBS[WF == W_MXFP8 ? st : 0][WF == W_MXFP8 ? 128 * wn + 32 * j + l32 : 0];
     }
   };
 
-  f32x4 acc[4][8];
+  // zero for FP8_B128; the pipelined formats' first step writes it without reading it
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int c0 = lane >> 4;  // operand chunk of this lane group (and c0 + 4)
-  const int ra = 64 * wm + (lane & 15), rb = 128 * wn + (lane & 15);
-
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
-  for (int s = 0; s < nk; ++s) {
-    const int st = s % kStages;
-    if (s + 1 < nk)
-      wait_vm<dmas_per_stage<WF>()>();
-    else
-      wait_vm<0>();
-    barrier();
-    if (s + 2 < nk) issue(s + 2);
-    const uint8_t* A_ = sA[st];
-    const uint8_t* B_ = sB[st];
-    if (WF == W_BF16) {
+  // MFMA m of a step (bf16 / MXFP8): K part outermost, so the two MFMAs on one
+  // accumulator are NI*4 instructions apart.  In the first step the first
+  // MFMA of each accumulator starts from zero (no zero-filled registers).
+  auto mfma_op = [&](int m, const Frag& f, auto ni_t, auto first_t) {
+    constexpr int NI = decltype(ni_t)::value;
+    const int kq = m / (NI * 4), i = (m / 4) % NI, j = m % 4;
+    f32x16 c = acc[i][j];
+    if (decltype(first_t)::value && kq == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(A_ + swz(ra + 16 * i, c0 + 4 * h));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(B_ + swz(rb + 16 * j, c0 + 4 * h));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
-        }
-      }
-    } else {
-      i32x8 a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(A_ + swz(ra + 16 * i, c0));
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(A_ + swz(ra + 16 * i, c0 + 4));
-        a[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      }
-      if (WF == W_MXFP8) {
-        int sa[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sa[i] = int((sAS[st][ra + 16 * i] >> (8 * c0)) & 0xffu);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(B_ + swz(rb + 16 * j, c0));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(B_ + swz(rb + 16 * j, c0 + 4));
-          const i32x8 b = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          const int sb = int((sBS[st][rb + 16 * j] >> (8 * c0)) & 0xffu);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, acc[i][j], 0, 0, 0, sa[i], 0, sb);
-        }
-      } else {  // FP8_B128: unit-scale MFMA per 128-deep block, promoted with sa * sb
-        const float w0 = sWs[wave][0][s + ks0], w1 = sWs[wave][1][s + ks0];
-        f32x4 fa[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[i] = *reinterpret_cast<const f32x4*>(&sAS[st][64 * wm + 16 * i + 4 * c0]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(B_ + swz(rb + 16 * j, c0));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(B_ + swz(rb + 16 * j, c0 + 4));
-          const i32x8 b = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          const float wj = (EPI == EPI_GATEUP && j >= 4) ? w1 : w0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
-                                                                              0, 0, 127, 0, 127);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) acc[i][j][k] = fmaf(t[k], fa[i][k] * wj, acc[i][j][k]);
-          }
-        }
-      }
+      for (int r = 0; r < 16; ++r) c[r] = 0.f;
     }
+    if constexpr (WF == W_BF16) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(get_slot(f.a[i][kq >> 1], kq)),
+                                                          as_bf16(get_slot(f.b[j][kq >> 1], kq)), c, 0, 0, 0);
+    } else {
+      const int sh = 8 * (2 * kq + g);
+      const int sa = int((f.sa[i] >> sh) & 0xffu), sb = int((f.sb[j] >> sh) & 0xffu);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i][kq], f.b[j][kq], c, 0, 0, 0, sa, 0, sb);
+    }
+  };
+
+  // ------------------------------------------------------------ main loop
+  const bool two = 64 * wm + 32 < mrows;  // this wave's second row block holds valid rows
+  if constexpr (WF == W_FP8_B128) {
+    auto run = [&](auto ni_t) {
+      constexpr int NI = decltype(ni_t)::value;
+      if (nk > 0) issue(0);
+      if (nk > 1) issue(1);
+      for (int s = 0; s < nk; ++s) {
+        const int st = s % kStages;
+        if (s + 1 < nk)
+          wait_vm<DPS>();
+        else
+          wait_vm<0>();
+        barrier();
+        if (s + 2 < nk) issue(s + 2);
+        Frag f;
+#pragma unroll
+        for (int r = 0; r < NI * 4 + 16; ++r) read_op(r, f, st, ni_t);
+        // activation scales of the lane's 16 output rows per block: rows 8q + 4g + [0, 4)
+        f32x4 fa[2][4];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            fa[i][q] = *reinterpret_cast<const f32x4*>(&sAS[st][64 * wm + 32 * i + 8 * q + 4 * g]);
+        const float w0 = sWs[wave][0][s + ks0], w1 = sWs[wave][1][s + ks0];
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {
+          f32x16 t[2][2];
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const int j = 2 * jh + jj;
+              f32x16 z;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) z[r] = 0.f;
+              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i][0], f.b[j][0], z, 0, 0, 0, 127, 0,
+                                                                         127);
+            }
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const int j = 2 * jh + jj;
+              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i][1], f.b[j][1], t[i][jj], 0, 0, 0,
+                                                                         127, 0, 127);
+            }
+          const float wj = (EPI == EPI_GATEUP && jh == 1) ? w1 : w0;
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                acc[i][2 * jh + jj][r] = fmaf(t[i][jj][r], fa[i][r / 4][r % 4] * wj, acc[i][2 * jh + jj][r]);
+        }
+      }
+    };
+    if (two)
+      run(IC<2>{});
+    else
+      run(IC<1>{});
+  } else {
+    auto run = [&](auto ni_t) {
+      constexpr int NI = decltype(ni_t)::value;
+      constexpr int NM = WF == W_BF16 ? NI * 16 : NI * 8;                // MFMAs per step
+      constexpr int NR = NI * 4 + 16 + (WF == W_MXFP8 ? NI + 4 : 0);     // LDS reads per step
+      // step s: MFMAs on cur (read during step s-1) interleaved with the reads
+      // of step s+1 into nxt and the direct-to-LDS loads of step s+3
+      // Every step issues its direct-to-LDS loads; past the last K step they
+      // reload the last step into a stage that is not read again (L2 hits),
+      // which keeps one instance of the step in the loop and every wait count
+      // fixed.
+      auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t) {
+        wait_lgkm0();  // cur is in registers: this wave no longer reads stage s
+        wait_vm<DPS>();  // this wave's loads of step s+1 have landed
+        barrier();       // ... and every wave's; stage s % 3 is free for step s+3
+        const int stn = (s + 1) % kStages, std_ = s % kStages;
+        const int kd = min(s + 3, nk - 1) + ks0;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mfma_op(m, cur, ni_t, first_t);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = (m * NR) / NM; r < ((m + 1) * NR) / NM; ++r) read_op(r, nxt, stn, ni_t);
+#pragma unroll
+          for (int d = (m * DPS) / NM; d < ((m + 1) * DPS) / NM; ++d) dma_op(d, std_, kd);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      Frag f0, f1;
+      issue(0);
+      issue(min(1, nk - 1));
+      issue(min(2, nk - 1));
+      wait_vm<2 * DPS>();
+      barrier();
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_op(r, f0, 0, ni_t);
+      step(0, f0, f1, std::true_type{});
+      int s = 1;
+      for (; s + 1 < nk; s += 2) {
+        step(s, f1, f0, std::false_type{});
+        step(s + 1, f0, f1, std::false_type{});
+      }
+      if (s < nk) step(s, f1, f0, std::false_type{});
+    };
+    if (nk > 0) run(IC<2>{});
   }
+  wait_vm<0>();
 
   // ------------------------------------------------------------ epilogue
-  // lane l holds rows 4(l/16)+k (k < 4) of each 16x16 tile, column l%16
-  const int col_l = lane & 15;
+  // lane l holds column l%32 of each 32x32 block, rows 8(r/4) + 4(l/32) + r%4
+  auto row_of = [&](int i, int r) { return 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3); };
+  if constexpr (EPI == EPI_GATEUP) {
+    // h = SiLU(g) * u in place of the gate blocks
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int rl = 64 * wm + 16 * i + 4 * c0 + k;
-      const bool rvalid = rl < mrows;
-      const size_t orow = size_t(seg0 + m0 + rl);
-      if (EPI == EPI_GATEUP) {
-        float h[4];
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = silu(acc[i][j][k]) * acc[i][j + 4][k];
-        const int cb = n0 + 64 * wn;  // first h column of this wave
-        if (p.C_f32) {
-          if (rvalid)
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = silu(acc[i][jj][r]) * acc[i][jj + 2][r];
+    const int cb = n0 + 64 * wn;  // first h column of this wave
+    if (p.C_f32 || p.out_afmt == A_NONE) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p.C_f32[orow * p.ldc + cb + 16 * j + col_l] = h[j];
-        } else if (p.out_afmt == A_NONE) {
-          if (rvalid)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              static_cast<uint16_t*>(p.C)[orow * p.ldc + cb + 16 * j + col_l] = f32_to_bf16(h[j]);
-        } else if (p.out_afmt == A_MXFP8_1X32) {  // block b = columns [32b, 32b+32) of this wave's 64
+        for (int r = 0; r < 16; ++r) {
+          const int rl = row_of(i, r);
+          if (rl >= mrows) continue;
+          const size_t o = size_t(seg0 + m0 + rl) * p.ldc + cb + l32;
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            float amax = fmaxf(fabsf(h[2 * b]), fabsf(h[2 * b + 1]));
-            amax = group_max<16>(amax);
-            const int xe = mx_exponent(amax);
-            if (rvalid) {
-#pragma unroll
-              for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * b + jj;
-                static_cast<uint8_t*>(p.C)[orow * p.ldc + cb + 16 * j + col_l] =
-                    uint8_t(f32_to_e4m3(__builtin_amdgcn_ldexpf(h[j], -xe)));
-              }
-              if (col_l == 0) static_cast<uint8_t*>(p.Cs)[orow * (p.N / 32) + cb / 32 + b] = uint8_t(xe + 127);
-            }
-          }
-        } else {  // A_FP8_1X128: the 128-column block spans both column waves
-          float amax = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(h[j]));
-          amax = group_max<16>(amax);
-          if (col_l == 0) sAmax[wn][rl] = amax;
-          __syncthreads();
-          amax = fmaxf(sAmax[0][rl], sAmax[1][rl]);
-          __syncthreads();
-          const float sc = amax > 0.f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
-          if (rvalid) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              static_cast<uint8_t*>(p.C)[orow * p.ldc + cb + 16 * j + col_l] = uint8_t(f32_to_e4m3(__fdiv_rn(h[j], sc)));
-            if (col_l == 0 && wn == 0) static_cast<float*>(p.Cs)[orow * (p.N / 128) + n0 / 128] = sc;
+          for (int jj = 0; jj < 2; ++jj) {
+            if (p.C_f32)
+              p.C_f32[o + 32 * jj] = acc[i][jj][r];
+            else
+              static_cast<uint16_t*>(p.C)[o + 32 * jj] = f32_to_bf16(acc[i][jj][r]);
           }
         }
-      } else {
-        if (!rvalid) continue;
+    } else if (p.out_afmt == A_MXFP8_1X32) {  // block jj = columns cb + [32jj, 32jj+32): one half wave
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = n0 + 128 * wn + 16 * j + col_l;
-          if (col < p.N) {
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = row_of(i, r);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const float amax = half_max(fabsf(acc[i][jj][r]));
+            const int xe = mx_exponent(amax);
+            if (rl < mrows) {
+              const size_t orow = size_t(seg0 + m0 + rl);
+              static_cast<uint8_t*>(p.C)[orow * p.ldc + cb + 32 * jj + l32] =
+                  uint8_t(f32_to_e4m3(__builtin_amdgcn_ldexpf(acc[i][jj][r], -xe)));
+              if (l32 == 0) static_cast<uint8_t*>(p.Cs)[orow * (N / 32) + cb / 32 + jj] = uint8_t(xe + 127);
+            }
+          }
+        }
+    } else {  // A_FP8_1X128: the 128-column block spans both column waves
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float amax = half_max(fmaxf(fabsf(acc[i][0][r]), fabsf(acc[i][1][r])));
+          if (l32 == 0) sAmax[wn][row_of(i, r)] = amax;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = row_of(i, r);
+          if (rl >= mrows) continue;
+          const float amax = fmaxf(sAmax[0][rl], sAmax[1][rl]);
+          const float sc = amax > 0.f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+          const size_t orow = size_t(seg0 + m0 + rl);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            static_cast<uint8_t*>(p.C)[orow * p.ldc + cb + 32 * jj + l32] =
+                uint8_t(f32_to_e4m3(__fdiv_rn(acc[i][jj][r], sc)));
+          if (l32 == 0 && wn == 0) static_cast<float*>(p.Cs)[orow * (N / 128) + n0 / 128] = sc;
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = row_of(i, r);
+        if (rl >= mrows) continue;
+        const size_t orow = size_t(seg0 + m0 + rl);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + 128 * wn + 32 * j + l32;
+          if (col < N) {
             if (EPI == EPI_F32)
-              static_cast<float*>(p.C)[kz * p.c_split + orow * p.ldc + col] = acc[i][j][k];
+              static_cast<float*>(p.C)[kz * p.c_split + orow * p.ldc + col] = acc[i][j][r];
             else
-              static_cast<uint16_t*>(p.C)[orow * p.ldc + col] = f32_to_bf16(acc[i][j][k]);
+              static_cast<uint16_t*>(p.C)[orow * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
           }
         }
       }
-    }
   }
 }
 
@@ -393,8 +467,13 @@ hipError_t launch_epi(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, hipStream_t s) {
+  if (gemm2_chosen(wfmt, epi, p)) return launch_gemm2(wfmt, epi, p, s);
   const int ntile = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
   if (ntile <= 0) return hipSuccess;
+  // the kernels address A rows and one group's B rows with 32-bit byte offsets
+  const long es = wfmt == W_BF16 ? 2 : 1;
+  const long a_rows = p.a_map ? (long(p.M) + p.a_div - 1) / p.a_div : long(p.M);
+  if (a_rows * p.lda * es >= (1L << 32) || long(p.N) * p.K * es >= (1L << 32)) return hipErrorInvalidValue;
   const int nper = epi == EPI_GATEUP ? BNT / 2 : BNT;
   const long tiles = long(ntile) * ((p.N + nper - 1) / nper) * (epi == EPI_F32 && p.ksplit > 1 ? p.ksplit : 1);
   const dim3 grid(unsigned((tiles + 7) / 8 * 8));  // the in-kernel schedule maps block b to XCD b % 8

@@ -1,0 +1,418 @@
+// Grouped GEMM, large-tile variant, for bf16 and MXFP8 weights (stages P1/P2
+// and Q1/Q2 of the DSV2-236B-MegaKernel README flowchart at batched sizes):
+//
+//   C[r][n] = sum_k A[r][k] * B_e[n][k]   for the rows r of expert e's segment
+//
+// Tile: 256 rows x 256 B rows, 64 bytes of K per step, 4 waves each owning
+// 128 x 128 (4 x 4 blocks of 32x32).  Measured on MI355X, a CU moves at most
+// about 64 bytes per clock from L2 into LDS or registers; this tile needs 32
+// bytes per clock at the full FP8 matrix rate (a 128 x 256 tile needs 47).
+// Four LDS stages of 32 KB, loaded four steps ahead with direct-to-LDS loads,
+// give three steps of memory latency slack.  Each lane keeps two register
+// sets of operands: the LDS reads of step s+1 and the loads of step s+4 are
+// issued among the MFMAs of step s in a fixed interleave.
+//
+//   bf16   v_mfma_f32_32x32x16_bf16, two per block per step
+//   MXFP8  v_mfma_scale_f32_32x32x64_f8f6f4, one per block per step, with the
+//          e8m0 scales of A and B per lane (lane l scales row l%32 for the
+//          32-deep K block l/32 of the instruction)
+//
+// LDS image: row r of a stage holds its 64 bytes as 4 chunks of 16, chunk c
+// at c ^ ((r >> 2) & 3), so the 16 lanes of one LDS read cycle (16 rows, one
+// chunk) hit 16 distinct bank groups.  Lane l's operand for a block is chunk
+// l/32 (bytes 0-15) and chunk 2 + l/32 (bytes 16-31) of row l%32: K bytes
+// [16g, 16g+16) and [32+16g, 48+16g), the instruction's K layout.
+//
+// MX scales (one e8m0 byte per 32 K of a row) are loaded once per 8 steps
+// (512 K): 16 bytes per row per load, into one of three LDS buffers, so the
+// scale loads add an eighth of the tile loads' cache-line requests instead of
+// matching them.  K must be a multiple of 512 (the host checks).
+//
+// EPI_GATEUP: B-tile rows [128w, 128w+64) are gate rows and [128w+64,
+// 128w+128) the up rows of the same 64 intermediate columns, so blocks j and
+// j+2 of a wave hold g and u of the same (row, column) and the epilogue writes
+// h = SiLU(g) * u, as bf16, fp32 or MXFP8 codes per 1x32 block ("From 35 to
+// 873 tokens/s", Rounds 12-15).  The other epilogues stage the fp32 / bf16
+// tile through LDS and store whole 16-byte row chunks.
+#include <algorithm>
+
+#include "gemm_dev.h"
+
+namespace moe {
+
+namespace {
+
+using namespace gemm_dev;
+
+constexpr int BM = kGemm2BM;  // 256 rows
+constexpr int BNT = 256;      // B rows per tile
+constexpr int BKB = 64;       // bytes of K per step
+constexpr int kStages = 4;
+constexpr int kLdsA = BM * BKB;   // 16 KB
+constexpr int kLdsB = BNT * BKB;  // 16 KB
+constexpr int kSG = 8;            // K steps per MX scale group (512 K)
+constexpr int kSBuf = 3;          // MX scale group buffers
+constexpr int kDPS = 8;           // tile loads per wave per step
+
+struct Frag {
+  i32x8 a[4];  // [32-row block i]: chunk g | chunk 2+g of the step's 64 bytes
+  i32x8 b[4];  // [32-row B block j]
+  uint32_t sa[4], sb[4];  // MXFP8: e8m0 byte of the lane's row for its K block
+};
+
+template <int WF, int EPI>
+__global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
+  constexpr bool MX = WF == W_MXFP8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * (kLdsA + kLdsB)];
+  __shared__ __attribute__((aligned(16))) uint8_t sS[MX ? kSBuf : 1][2][MX ? BM * 16 : 16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 5, l32 = lane & 31;
+  constexpr int nper = EPI == EPI_GATEUP ? BNT / 2 : BNT;  // output columns per tile
+  const int KS = (EPI == EPI_F32 && p.ksplit > 1) ? p.ksplit : 1;
+  const Tile tl = tile_of(p, BM, nper, KS);
+  if (!tl.valid) return;
+  const int e = tl.e, m0 = tl.m0, n0 = tl.n0, seg0 = tl.seg0, mrows = tl.mrows, kz = tl.kz;
+  const int K = p.K, N = p.N;
+  const int nk_all = K * esz<WF>() / BKB;
+  const int ks0 = int(long(nk_all) * kz / KS), ks1 = int(long(nk_all) * (kz + 1) / KS);
+  const int nk = ks1 - ks0;  // K steps of this slice, starting at step ks0
+  if (nk <= 0) return;
+  const uint32_t lda_b = uint32_t(p.lda) * esz<WF>();
+  const uint32_t ldb_b = uint32_t(K) * esz<WF>();
+
+  const int* a_map = p.a_map;
+  const int a_div = p.a_div;
+  const int rbase = seg0 + m0, rlast = mrows - 1;
+#define PHYS_ROW(rl) uint32_t(a_map ? a_map[rbase + min((rl), rlast)] / a_div : rbase + min((rl), rlast))
+
+  // ---------------------------------------------------------- load sources
+  // A: wave w loads tile rows [64w, 64w+64) as 4 blocks of 16; lane L fetches
+  // row 16k + L/4 of block k, chunk (L%4) ^ ((row>>2)&3).
+  const uint8_t* a_base = uniform_ptr(p.A);
+  uint32_t oa[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 64 * wave + 16 * k + (lane >> 2);
+    oa[k] = PHYS_ROW(r) * lda_b + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+  }
+  // B: wave w loads tile B rows [64w, 64w+64); for EPI_GATEUP these are gate
+  // rows (w even) or up rows (w odd) of intermediate columns n0 + 64 (w/2) + [0, 64)
+  const uint8_t* b_base;
+  uint32_t ob[4];
+  {
+    const void* bsrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1 : p.B0;
+    b_base = uniform_ptr(static_cast<const uint8_t*>(bsrc) + size_t(e) * p.b_stride * esz<WF>());
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = 64 * wave + 16 * k + (lane >> 2);
+      const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + 16 * k + (lane >> 2) : min(n0 + t, N - 1);
+      ob[k] = uint32_t(br) * ldb_b + (((lane & 3) ^ ((t >> 2) & 3)) << 4);
+    }
+  }
+  // MX scales: wave w loads the 16 bytes of A rows and B rows [64w, 64w+64) of a group
+  const uint8_t* as_base = nullptr;
+  const uint8_t* bs_base = nullptr;
+  uint32_t oas = 0, obs = 0;
+  if constexpr (MX) {
+    as_base = uniform_ptr(p.As);
+    oas = PHYS_ROW(64 * wave + lane) * uint32_t(K / 32);
+    const void* ssrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1s : p.B0s;
+    bs_base = uniform_ptr(static_cast<const uint8_t*>(ssrc) + size_t(e) * p.bs_stride);
+    const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + lane : min(n0 + 64 * wave + lane, N - 1);
+    obs = uint32_t(br) * uint32_t(K / 32);
+  }
+#undef PHYS_ROW
+
+  const uint32_t lds_a0 = lds_addr(smem), lds_b0 = lds_a0 + kStages * kLdsA;
+  const int ngroups = (nk + kSG - 1) / kSG;
+  auto tile_dma = [&](int d, int st, int kstep) {
+    if (d < 4)
+      dma16(oa[d], a_base + size_t(kstep) * BKB, lds_a0 + st * kLdsA + (64 * wave + 16 * d) * BKB);
+    else
+      dma16(ob[d - 4], b_base + size_t(kstep) * BKB, lds_b0 + st * kLdsB + (64 * wave + 16 * (d - 4)) * BKB);
+  };
+  auto scale_dma = [&](int q) {  // scale group q (clamped) into buffer q % 3
+    const int qq = min(q, ngroups - 1), buf = q % kSBuf;
+    dma16(oas, as_base + 16 * qq, lds_addr(&sS[buf][0][64 * wave * 16]));
+    dma16(obs, bs_base + 16 * qq, lds_addr(&sS[buf][1][64 * wave * 16]));
+  };
+
+  // LDS operand reads: block i of the lane's rows, chunks g and 2+g
+  const int f = (l32 >> 2) & 3;
+  const int colo0 = (g ^ f) << 4, colo1 = ((2 + g) ^ f) << 4;
+  const int rowA = (128 * wm + l32) * BKB, rowB = (128 * wn + l32) * BKB;
+  const int srowA = (128 * wm + l32) * 16 + g, srowB = (128 * wn + l32) * 16 + g;
+  constexpr int NR = 16 + (MX ? 8 : 0);  // LDS reads per step
+  auto read_op = [&](int r, Frag& fr, int t) {  // read r of step t's operands
+    const int st = t % kStages;
+    const uint8_t* As_ = smem + st * kLdsA;
+    const uint8_t* Bs_ = smem + kStages * kLdsA + st * kLdsB;
+    if (r < 8) {
+      const int i = r / 2;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(As_ + rowA + 32 * BKB * i + ((r & 1) ? colo1 : colo0));
+      if (r & 1)
+        fr.a[i].hi = v;
+      else
+        fr.a[i].lo = v;
+    } else if (r < 16) {
+      const int j = (r - 8) / 2;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(Bs_ + rowB + 32 * BKB * j + ((r & 1) ? colo1 : colo0));
+      if (r & 1)
+        fr.b[j].hi = v;
+      else
+        fr.b[j].lo = v;
+    } else if constexpr (MX) {
+      const int buf = (t / kSG) % kSBuf, byte = 2 * (t % kSG);
+      if (r < 20)
+        fr.sa[r - 16] = sS[buf][0][srowA + 32 * 16 * (r - 16) + byte];
+      else
+        fr.sb[r - 20] = sS[buf][1][srowB + 32 * 16 * (r - 20) + byte];
+    }
+  };
+
+  // rows of this wave's blocks that hold valid rows: blocks at or past nI are skipped
+  const int nI = min(max((mrows - 128 * wm + 31) / 32, 0), 4);
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // MFMA m of a step.  bf16: K half outermost, so the two MFMAs on one
+  // accumulator are 16 instructions apart.  In the first step each
+  // accumulator's first MFMA starts from zero.
+  constexpr int NM = MX ? 16 : 32;
+  auto mfma_op = [&](int m, const Frag& fr, auto first_t) {
+    const int q = m / 16, i = (m / 4) % 4, j = m % 4;
+    if (i >= nI) return;
+    f32x16 c = acc[i][j];
+    if (decltype(first_t)::value && q == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[r] = 0.f;
+    }
+    if constexpr (MX) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr.a[i], fr.b[j], c, 0, 0, 0, int(fr.sa[i]), 0,
+                                                                  int(fr.sb[j]));
+    } else {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(q ? fr.a[i].hi : fr.a[i].lo),
+                                                          as_bf16(q ? fr.b[j].hi : fr.b[j].lo), c, 0, 0, 0);
+    }
+  };
+
+  // step s: MFMAs on cur (read during step s-1) interleaved with the LDS reads
+  // of step s+1 into nxt and the loads of step s+4 into stage s % 4.  Past the
+  // last K step the loads repeat the last step into stages nothing reads again,
+  // so every step issues the same loads and the wait counts stay fixed.
+  auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t) {
+    wait_lgkm0();  // cur is in registers: this wave no longer reads stage s
+    // this wave's loads of step s+1 have landed: the loads of steps s-2 and s-1
+    // may still be in flight (8 each, plus 2 scale loads issued at steps = 0 mod 8)
+    const int sm = s & (kSG - 1);
+    if (MX && (sm == 1 || sm == 2))
+      wait_vm<2 * kDPS + 2>();
+    else
+      wait_vm<2 * kDPS>();
+    barrier();  // ... and every wave's; stage s % 4 is free for step s+4
+    if (MX && sm == 0) scale_dma(s / kSG + 1);
+    const int kd = min(s + kStages, nk - 1) + ks0, std_ = s % kStages;
+    // the reads go among the first half of the MFMAs, so they have landed
+    // when the next step starts; the loads go among the second half
+    constexpr int NH = NM / 2;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mfma_op(m, cur, first_t);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m < NH) {
+#pragma unroll
+        for (int r = (m * NR) / NH; r < ((m + 1) * NR) / NH; ++r) read_op(r, nxt, s + 1);
+      } else {
+#pragma unroll
+        for (int d = ((m - NH) * kDPS) / NH; d < ((m - NH + 1) * kDPS) / NH; ++d) tile_dma(d, std_, kd);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ------------------------------------------------------------ main loop
+  Frag f0, f1;
+  if constexpr (MX) scale_dma(0);
+#pragma unroll
+  for (int t = 0; t < kStages; ++t)
+#pragma unroll
+    for (int d = 0; d < kDPS; ++d) tile_dma(d, t, min(t, nk - 1) + ks0);
+  wait_vm<(kStages - 1) * kDPS>();
+  barrier();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read_op(r, f0, 0);
+  step(0, f0, f1, std::true_type{});
+  int s = 1;
+  for (; s + 1 < nk; s += 2) {
+    step(s, f1, f0, std::false_type{});
+    step(s + 1, f0, f1, std::false_type{});
+  }
+  if (s < nk) step(s, f1, f0, std::false_type{});
+  wait_vm<0>();
+  wait_lgkm0();
+  barrier();  // the stages are free for the epilogue
+
+  // ------------------------------------------------------------ epilogue
+  // lane l holds column l%32 of each 32x32 block, rows 8(r/4) + 4(l/32) + r%4
+  auto row_of = [&](int i, int r) { return 128 * wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3); };
+  if constexpr (EPI == EPI_GATEUP) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = silu(acc[i][jj][r]) * acc[i][jj + 2][r];
+    // Stage the wave's h (128 rows x 64 columns, fp32) through LDS, 64 rows
+    // at a time, so that each lane finishes whole 32-column row blocks in
+    // registers: the MX block maximum without cross-lane reductions, and
+    // 16-byte stores.  One wave writes and reads its own region; its LDS
+    // operations complete in order.
+    constexpr int RSF = 68;  // floats per staged row (64 + 4: conflict-free 16-byte reads)
+    float* wsf = reinterpret_cast<float*>(smem) + wave * (64 * RSF);
+    const int cb = n0 + 64 * wn;  // first h column of this wave
+    const int omode = p.C_f32 ? 0 : (p.out_afmt == A_NONE ? 1 : 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            wsf[(32 * ii + 8 * (r >> 2) + 4 * g + (r & 3)) * RSF + 32 * jj + l32] = acc[2 * h + ii][jj][r];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int b = lane + 64 * k, row = b >> 1, half = b & 1;
+        const int rl = 128 * wm + 64 * h + row;
+        f32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const f32x4*>(wsf + row * RSF + 32 * half + 4 * q);
+        if (rl >= mrows) continue;
+        const size_t orow = size_t(seg0 + m0 + rl);
+        const int col = cb + 32 * half;
+        if (omode == 0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) *reinterpret_cast<f32x4*>(p.C_f32 + orow * p.ldc + col + 4 * q) = v[q];
+        } else if (omode == 1) {
+          uint16_t* dst = static_cast<uint16_t*>(p.C) + orow * p.ldc + col;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            i32x4 o;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const f32x4& x = v[2 * q + t / 2];
+              const int c = 2 * (t & 1);
+              o[t] = int(uint32_t(f32_to_bf16(x[c])) | (uint32_t(f32_to_bf16(x[c + 1])) << 16));
+            }
+            *reinterpret_cast<i32x4*>(dst + 8 * q) = o;
+          }
+        } else {  // MXFP8 1x32: this lane's 32 values are one block
+          float amax = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[q][0]), fabsf(v[q][1])), fmaxf(fabsf(v[q][2]), fabsf(v[q][3]))));
+          const int xe = mx_exponent(amax);
+          uint8_t* dst = static_cast<uint8_t*>(p.C) + orow * p.ldc + col;
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            i32x4 o;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const f32x4& x = v[4 * q2 + t];
+              o[t] = int(e4m3x4_sat(__builtin_amdgcn_ldexpf(x[0], -xe), __builtin_amdgcn_ldexpf(x[1], -xe),
+                                    __builtin_amdgcn_ldexpf(x[2], -xe), __builtin_amdgcn_ldexpf(x[3], -xe)));
+            }
+            *reinterpret_cast<i32x4*>(dst + 16 * q2) = o;
+          }
+          static_cast<uint8_t*>(p.Cs)[orow * (N / 32) + col / 32] = uint8_t(xe + 127);
+        }
+      }
+    }
+  } else {
+    // stage the wave's 128 x 128 block through LDS, one 32-row block at a
+    // time (at most 4 x 32 x 528 bytes), and store whole 16-byte row chunks
+    constexpr int ES = EPI == EPI_F32 ? 4 : 2;
+    constexpr int RS = 128 * ES + 16;  // LDS row stride (bytes), padded
+    constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row
+    uint8_t* ws = smem + wave * (32 * RS);
+    const int cw = n0 + 128 * wn;  // first output column of this wave
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          uint8_t* d = ws + (8 * (r >> 2) + 4 * g + (r & 3)) * RS + (32 * j + l32) * ES;
+          if (EPI == EPI_F32)
+            *reinterpret_cast<float*>(d) = acc[i][j][r];
+          else
+            *reinterpret_cast<uint16_t*>(d) = f32_to_bf16(acc[i][j][r]);
+        }
+#pragma unroll 4
+      for (int c = lane; c < 32 * CPR; c += 64) {
+        const int rl = c / CPR, cc = c % CPR;
+        const int row = 128 * wm + 32 * i + rl;
+        if (row >= mrows) continue;
+        const int col = cw + cc * (16 / ES);
+        const i32x4 v = *reinterpret_cast<const i32x4*>(ws + rl * RS + cc * 16);
+        const size_t orow = size_t(seg0 + m0 + row);
+        uint8_t* dst = static_cast<uint8_t*>(p.C) + (size_t(kz) * p.c_split + orow * p.ldc + col) * ES;
+        if (col + 16 / ES <= N) {
+          *reinterpret_cast<i32x4*>(dst) = v;
+        } else {
+          for (int q = 0; q < 16 / ES && col + q < N; ++q)
+            for (int b = 0; b < ES; ++b) dst[q * ES + b] = reinterpret_cast<const uint8_t*>(&v)[q * ES + b];
+        }
+      }
+    }
+  }
+}
+
+template <int WF>
+hipError_t launch_epi(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL((gemm2_kernel<WF, EPI_F32>), grid, dim3(256), 0, s, p); break;
+    case EPI_BF16: hipLaunchKernelGGL((gemm2_kernel<WF, EPI_BF16>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((gemm2_kernel<WF, EPI_GATEUP>), grid, dim3(256), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm2_serves(int wfmt, int K, int epi, int out_afmt, int ksplit) {
+  if (wfmt == W_BF16) return epi != EPI_GATEUP || out_afmt == A_NONE;
+  if (wfmt == W_MXFP8) return K % 512 == 0 && ksplit <= 1 && (epi != EPI_GATEUP || out_afmt != A_FP8_1X128);
+  return false;
+}
+
+bool gemm2_chosen(int wfmt, int epi, const GemmParams& p) {
+  if (p.tiles) return p.bm == kGemm2BM;
+  if (!gemm2_serves(wfmt, p.K, epi, p.C_f32 ? A_NONE : p.out_afmt, p.ksplit)) return false;
+  const int nper = epi == EPI_GATEUP ? BNT / 2 : BNT;
+  const long t2 = long((p.M + BM - 1) / BM) * ((p.N + nper - 1) / nper) * std::max(p.ksplit, 1);
+  return t2 >= 224;  // about the CU count: fewer large tiles would leave CUs idle
+}
+
+hipError_t launch_gemm2(int wfmt, int epi, const GemmParams& p, hipStream_t s) {
+  const int ntile = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
+  if (ntile <= 0) return hipSuccess;
+  if (!gemm2_serves(wfmt, p.K, epi, p.C_f32 ? A_NONE : p.out_afmt, p.ksplit)) return hipErrorInvalidValue;
+  // the kernels address A rows and one group's B rows with 32-bit byte offsets
+  const long es = wfmt == W_BF16 ? 2 : 1;
+  const long a_rows = p.a_map ? (long(p.M) + p.a_div - 1) / p.a_div : long(p.M);
+  if (a_rows * p.lda * es >= (1L << 32) || long(p.N) * p.K * es >= (1L << 32)) return hipErrorInvalidValue;
+  const int nper = epi == EPI_GATEUP ? BNT / 2 : BNT;
+  const long tiles = long(ntile) * ((p.N + nper - 1) / nper) * (epi == EPI_F32 && p.ksplit > 1 ? p.ksplit : 1);
+  const dim3 grid(unsigned((tiles + 7) / 8 * 8));  // the in-kernel schedule maps block b to XCD b % 8
+  return wfmt == W_BF16 ? launch_epi<W_BF16>(epi, p, grid, s) : launch_epi<W_MXFP8>(epi, p, grid, s);
+}
+
+}  // namespace moe

@@ -81,10 +81,26 @@ struct GemmParams {
   // z writes its partial product to C + z * c_split (elements)
   int ksplit;
   long c_split;
+  // rows per tile the tile list was built for: kGemm2BM selects the large-tile
+  // kernel (gemm2.hip), anything else the 128-row kernel (gemm.hip).  Without
+  // a tile list the launcher picks the kernel (gemm2_chosen).
+  int bm;
 };
 constexpr int kGemmBM = 128;
+constexpr int kGemm2BM = 256;
 constexpr int kGemmMaxK = 8192;  // FP8_B128 GEMM: K (elements) <= this
 hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, hipStream_t s);
+// large-tile kernel: bf16, and MXFP8 with K a multiple of 512
+bool gemm2_serves(int wfmt, int K, int epi, int out_afmt, int ksplit);
+// whether launch_gemm runs p on the large-tile kernel: with a tile list when it
+// was built for kGemm2BM; without one when that kernel serves the format and
+// its tiles still fill the chip
+bool gemm2_chosen(int wfmt, int epi, const GemmParams& p);
+hipError_t launch_gemm2(int wfmt, int epi, const GemmParams& p, hipStream_t s);
+// rows per tile of an expert FFN's two GEMMs (gate/up with K = H, down with K = I)
+inline int ffn_tile_rows(int wfmt, int H, int I) {
+  return (wfmt == W_BF16 || (wfmt == W_MXFP8 && H % 512 == 0 && I % 512 == 0)) ? kGemm2BM : kGemmBM;
+}
 
 // ------------------------------------------------------------------ small-batch GEMV FFN
 struct GemvUpParams {
