@@ -372,65 +372,92 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][jj][r] = silu(acc[i][jj][r]) * acc[i][jj + 2][r];
-    const int cb = n0 + 64 * wn;  // first h column of this wave
-    if (p.C_f32 || p.out_afmt == A_NONE) {
+    // Stage the tile's h (128 rows x 128 columns, fp32) through LDS, so that
+    // each thread finishes 64 columns of one row in registers: block maxima
+    // without cross-lane reductions (a 1x128 block is two threads, combined
+    // through LDS), the hardware e4m3 pack, and 16-byte stores.
+    constexpr int RSF = 132;  // floats per staged row: 16-byte reads of 16 consecutive rows hit distinct banks
+    float* hb = reinterpret_cast<float*>(smem);
+    wait_vm<0>();
+    __syncthreads();  // every wave is done with the stages
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = row_of(i, r);
-          if (rl >= mrows) continue;
-          const size_t o = size_t(seg0 + m0 + rl) * p.ldc + cb + l32;
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            if (p.C_f32)
-              p.C_f32[o + 32 * jj] = acc[i][jj][r];
-            else
-              static_cast<uint16_t*>(p.C)[o + 32 * jj] = f32_to_bf16(acc[i][jj][r]);
-          }
-        }
-    } else if (p.out_afmt == A_MXFP8_1X32) {  // block jj = columns cb + [32jj, 32jj+32): one half wave
+        for (int r = 0; r < 16; ++r) hb[row_of(i, r) * RSF + 64 * wn + 32 * jj + l32] = acc[i][jj][r];
+    __syncthreads();
+    const int row = tid & 127, half = tid >> 7;  // this thread: h columns n0 + 64 half + [0, 64) of tile row `row`
+    f32x4 v[16];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int q4 = 0; q4 < 16; ++q4) v[q4] = *reinterpret_cast<const f32x4*>(hb + row * RSF + 64 * half + 4 * q4);
+    float m = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = row_of(i, r);
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const float amax = half_max(fabsf(acc[i][jj][r]));
-            const int xe = mx_exponent(amax);
-            if (rl < mrows) {
-              const size_t orow = size_t(seg0 + m0 + rl);
-              static_cast<uint8_t*>(p.C)[orow * p.ldc + cb + 32 * jj + l32] =
-                  uint8_t(f32_to_e4m3(__builtin_amdgcn_ldexpf(acc[i][jj][r], -xe)));
-              if (l32 == 0) static_cast<uint8_t*>(p.Cs)[orow * (N / 32) + cb / 32 + jj] = uint8_t(xe + 127);
-            }
-          }
-        }
-    } else {  // A_FP8_1X128: the 128-column block spans both column waves
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float amax = half_max(fmaxf(fabsf(acc[i][0][r]), fabsf(acc[i][1][r])));
-          if (l32 == 0) sAmax[wn][row_of(i, r)] = amax;
-        }
+    for (int q4 = 0; q4 < 16; ++q4)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[q4][0]), fabsf(v[q4][1])), fmaxf(fabsf(v[q4][2]), fabsf(v[q4][3]))));
+    if (!p.C_f32 && p.out_afmt == A_FP8_1X128) {  // the 128-column block is both halves of the row
+      sAmax[half][row] = m;
       __syncthreads();
+      m = fmaxf(sAmax[0][row], sAmax[1][row]);
+    }
+    if (row < mrows) {
+      const size_t orow = size_t(seg0 + m0 + row);
+      const int col = n0 + 64 * half;
+      if (p.C_f32) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int q4 = 0; q4 < 16; ++q4) *reinterpret_cast<f32x4*>(p.C_f32 + orow * p.ldc + col + 4 * q4) = v[q4];
+      } else if (p.out_afmt == A_NONE) {
+        uint16_t* dst = static_cast<uint16_t*>(p.C) + orow * p.ldc + col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = row_of(i, r);
-          if (rl >= mrows) continue;
-          const float amax = fmaxf(sAmax[0][rl], sAmax[1][rl]);
-          const float sc = amax > 0.f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
-          const size_t orow = size_t(seg0 + m0 + rl);
+        for (int q8 = 0; q8 < 8; ++q8) {
+          i32x4 o;
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            static_cast<uint8_t*>(p.C)[orow * p.ldc + cb + 32 * jj + l32] =
-                uint8_t(f32_to_e4m3(__fdiv_rn(acc[i][jj][r], sc)));
-          if (l32 == 0 && wn == 0) static_cast<float*>(p.Cs)[orow * (N / 128) + n0 / 128] = sc;
+          for (int t = 0; t < 4; ++t) {
+            const f32x4& x = v[2 * q8 + t / 2];
+            const int cc = 2 * (t & 1);
+            o[t] = int(uint32_t(f32_to_bf16(x[cc])) | (uint32_t(f32_to_bf16(x[cc + 1])) << 16));
+          }
+          *reinterpret_cast<i32x4*>(dst + 8 * q8) = o;
         }
+      } else {
+        uint8_t* dst = static_cast<uint8_t*>(p.C) + orow * p.ldc + col;
+        if (p.out_afmt == A_MXFP8_1X32) {  // two 1x32 blocks: columns [32b, 32b+32)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            float am = 0.f;
+#pragma unroll
+            for (int q4 = 8 * b; q4 < 8 * b + 8; ++q4)
+              am = fmaxf(am, fmaxf(fmaxf(fabsf(v[q4][0]), fabsf(v[q4][1])), fmaxf(fabsf(v[q4][2]), fabsf(v[q4][3]))));
+            const int xe = mx_exponent(am);
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+              i32x4 o;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const f32x4& x = v[8 * b + 4 * q2 + t];
+                o[t] = int(e4m3x4_sat(__builtin_amdgcn_ldexpf(x[0], -xe), __builtin_amdgcn_ldexpf(x[1], -xe),
+                                      __builtin_amdgcn_ldexpf(x[2], -xe), __builtin_amdgcn_ldexpf(x[3], -xe)));
+              }
+              *reinterpret_cast<i32x4*>(dst + 32 * b + 16 * q2) = o;
+            }
+            static_cast<uint8_t*>(p.Cs)[orow * (N / 32) + col / 32 + b] = uint8_t(xe + 127);
+          }
+        } else {  // 1x128: s = fl32(amax / 448), codes of fl32(v / s)
+          const float sc = m > 0.f ? __fdiv_rn(m, kE4M3Max) : 1.0f;
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            i32x4 o;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const f32x4& x = v[4 * q2 + t];
+              o[t] = int(e4m3x4_sat(__fdiv_rn(x[0], sc), __fdiv_rn(x[1], sc), __fdiv_rn(x[2], sc),
+                                    __fdiv_rn(x[3], sc)));
+            }
+            *reinterpret_cast<i32x4*>(dst + 16 * q2) = o;
+          }
+          if (half == 0) static_cast<float*>(p.Cs)[orow * (N / 128) + n0 / 128] = sc;
+        }
+      }
     }
   } else {
 #pragma unroll

@@ -71,34 +71,33 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     return;
   }
 
-  uint32_t code[8];
+  float a[8];  // the values divided by the block scale, then encoded with e4m3x4_sat
   float scale;
   if (AF == A_FP8_1X128) {
     amax = group_max<16>(amax);
     scale = amax > 0.f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = f32_to_e4m3(__fdiv_rn(v[i], scale));
+    for (int i = 0; i < 8; ++i) a[i] = __fdiv_rn(v[i], scale);
   } else {
     amax = group_max<4>(amax);
     const int xe = mx_exponent(amax);
     scale = __builtin_amdgcn_ldexpf(1.0f, xe);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = f32_to_e4m3(__builtin_amdgcn_ldexpf(v[i], -xe));
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_amdgcn_ldexpf(v[i], -xe);
     if (active && (lane & 3) == 0 && !deq)
       static_cast<uint8_t*>(qs)[size_t(r) * (H / 32) + c / 32] = uint8_t(xe + 127);
   }
   if (!active) return;
+  const uint32_t lo = e4m3x4_sat(a[0], a[1], a[2], a[3]), hi = e4m3x4_sat(a[4], a[5], a[6], a[7]);
   if (deq) {
     float d[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = dec1(code[i]) * scale;
+    for (int i = 0; i < 8; ++i) d[i] = dec1(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xffu) * scale;
     float4* o = reinterpret_cast<float4*>(deq + size_t(r) * H + c);
     o[0] = make_float4(d[0], d[1], d[2], d[3]);
     o[1] = make_float4(d[4], d[5], d[6], d[7]);
     return;
   }
-  uint32_t lo = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-  uint32_t hi = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
   *reinterpret_cast<uint2*>(static_cast<uint8_t*>(q) + size_t(r) * H + c) = make_uint2(lo, hi);
   if (AF == A_FP8_1X128 && (lane & 15) == 0) static_cast<float*>(qs)[size_t(r) * (H / 128) + c / 128] = scale;
 }
@@ -122,7 +121,7 @@ __global__ void e4m3_decode_kernel(const uint8_t* codes, float* out, int n) {
 }
 __global__ void e4m3_encode_kernel(const float* in, uint8_t* codes, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) codes[i] = uint8_t(f32_to_e4m3(in[i]));
+  if (i < n) codes[i] = uint8_t(e4m3x4_sat(in[i], 0.f, 0.f, 0.f) & 0xffu);  // the quantisers' encoder
 }
 
 template <bool IN_F32>
