@@ -92,7 +92,7 @@ size_t wscale_stride(int wfmt, int N, int K) {  // scale elements per expert
 }
 
 struct Ws {
-  size_t counter, logits, ids, w, offsets, perm, inv, tiles, ntiles;
+  size_t counter, logits, ids, w, offsets, perm, inv, hist, tiles, ntiles;
   size_t xq, xqs, xs2, xs2s;  // routed-format x, shared-format x
   size_t h, hs, hsh, hshs;    // routed h (+scales), shared h (+scales)
   size_t yperm, ysh;
@@ -117,6 +117,7 @@ Ws plan(const moe_config* c, int Tm) {
   s.offsets = take((E + 1) * 4);
   s.perm = take(TK * 4);
   s.inv = take(TK * 4);
+  s.hist = take(permute_hist_ints(int(TK), int(E)) * 4);
   s.tiles = take(size_t(2) * max_tiles(int(TK), int(E), kGemmBM) * 4);
   s.ntiles = take(16);
   // x in the routed activation format: quantised rows (up to TK rows for
@@ -312,7 +313,7 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
   const Ws L = plan(cfg, T);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
   const int TK = T * cfg->topk;
-  LAUNCH("permute", launch_permute(topk_ids, TK, cfg->n_experts, expert_offsets, perm_src, inv_pos, nullptr, nullptr, kGemmBM,
+  LAUNCH("permute", launch_permute(topk_ids, TK, cfg->n_experts, at<int>(ws, L.hist), expert_offsets, perm_src, inv_pos, nullptr, nullptr, kGemmBM,
                          stream));
   if (x_perm)
     LAUNCH("quant_rows", launch_quant_rows(x, false, TK, cfg->hidden, perm_src, cfg->topk, cfg->routed_afmt, x_perm, x_perm_scale,
@@ -649,7 +650,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   int* tiles = at<int>(ws, L.tiles);
   int* ntiles = at<int>(ws, L.ntiles);
   const int rbm = ffn_tile_rows(cfg->routed_wfmt, H, cfg->inter);
-  LAUNCH("permute", launch_permute(ids, TK, E, off, perm, inv, tiles, ntiles, rbm, stream));
+  LAUNCH("permute", launch_permute(ids, TK, E, at<int>(ws, L.hist), off, perm, inv, tiles, ntiles, rbm, stream));
   const void* xa = x;
   const void* xas = nullptr;
   if (raf != A_NONE) {

@@ -29,7 +29,9 @@ constexpr int kRouterMaxSplit = 16;  // K slices of the batched router GEMM
 // ids [TK]; writes offsets [E+1], perm_src [TK], inv_pos [TK]; when tiles is
 // non-null also the grouped-GEMM tile list for row tiles of `bm` rows:
 // tiles[2i] = expert, tiles[2i+1] = row offset in the segment; ntiles[0] = count.
-hipError_t launch_permute(const int* ids, int TK, int E, int* offsets, int* perm_src, int* inv_pos,
+// hist: int32 scratch of permute_hist_ints(TK, E) entries.
+constexpr size_t permute_hist_ints(int TK, int E) { return size_t((TK + 1023) / 1024) * size_t(E); }
+hipError_t launch_permute(const int* ids, int TK, int E, int* hist, int* offsets, int* perm_src, int* inv_pos,
                           int* tiles, int* ntiles, int bm, hipStream_t s);
 hipError_t launch_build_tiles(const int* offsets, int E, int rows, int bm, int* tiles, int* ntiles, hipStream_t s);
 inline int max_tiles(int rows, int E, int bm) { return (rows + bm - 1) / bm + E; }

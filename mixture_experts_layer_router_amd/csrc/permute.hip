@@ -2,13 +2,16 @@
 // GPU and without any host round trip (Mixture-of-Kittens, Abstract and
 // Figure 1: GPU-side dispatch scheduling, no CPU-GPU synchronisation).
 //
-// One workgroup of 1024 threads: a histogram, an exclusive scan over the
-// experts, then a stable scatter in chunks of 1024 slots.  Within a wave, the
-// slots of one expert are found with ballots (an 8-bit bit-sliced match), so
-// the histogram takes one LDS add per (wave, expert) instead of one per slot,
-// and a slot's rank among equal experts is a popcount; per chunk, one thread
-// per expert turns the waves' counts into each wave's first position.  The
-// order is the flat slot order: integer-only and deterministic.
+// Two launches over chunks of 1024 slots, one workgroup per chunk: each
+// chunk's per-expert counts, then a stable scatter in which every workgroup
+// reduces those counts itself (expert totals, the counts of the chunks before
+// its own, an exclusive scan over the experts), so no workgroup ever waits for
+// another.  Within a wave, the slots of one expert are found with ballots (an
+// 8-bit bit-sliced match): the count takes one LDS add per (wave, expert)
+// instead of one per slot, and a slot's rank among equal experts is a
+// popcount; one 16-lane row per expert turns the waves' counts into each
+// wave's first position.  The order is the flat slot order: integer-only and
+// deterministic.  A single chunk needs only the second launch.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,7 +21,7 @@ namespace {
 
 constexpr int kMaxE = 256;
 constexpr int kWaves = 16;  // one row of 16 lanes covers an expert's per-wave counts
-constexpr int kGroup = 24;  // chunks of 1024 slots whose ids a thread holds at once
+constexpr int kChunk = 1024;  // slots per workgroup, one per thread
 
 MOE_DEV int wave_incl_scan(int v) {
   const int lane = lane_id();
@@ -86,15 +89,6 @@ MOE_DEV void write_tiles(const int* cnt, int E, int bm, int* tiles, int* ntiles,
   }
 }
 
-// Workgroup barrier for LDS traffic only: __syncthreads() also waits for the
-// thread's outstanding global stores (a workgroup-scope release), which in the
-// chunk loop would put the store latency of every chunk on the critical path.
-MOE_DEV void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // inclusive prefix sum over each row of 16 lanes (DPP row shifts; lanes
 // shifted in from outside the row add 0)
 MOE_DEV int row16_incl_scan(int v) {
@@ -118,87 +112,88 @@ MOE_DEV uint64_t same_expert_lanes(int e, bool valid) {
   return m;
 }
 
-__global__ __launch_bounds__(1024) void permute_kernel(const int* __restrict__ ids, int TK, int E,
-                                                       int* __restrict__ offsets, int* __restrict__ perm_src,
-                                                       int* __restrict__ inv_pos, int* tiles, int* ntiles,
-                                                       int bm) {
+// Per-chunk expert counts: chunk c (1024 slots) writes hist[c][0..E).
+__global__ __launch_bounds__(1024) void permute_count_kernel(const int* __restrict__ ids, int TK, int E,
+                                                             int* __restrict__ hist) {
   __shared__ int cnt[kMaxE];
-  __shared__ int base[kMaxE];
-  __shared__ int wcnt[kMaxE][kWaves];  // this chunk's count per (expert, wave)
-  __shared__ int wpre[kMaxE][kWaves];  // ... and the position of its first slot
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < kMaxE; i += 1024) cnt[i] = 0;
-  for (int i = tid; i < kWaves * kMaxE; i += 1024) (&wcnt[0][0])[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, c = blockIdx.x;
+  const int p = c * kChunk + tid;
+  const int e = p < TK ? ids[p] : -1;
+  const bool valid = e >= 0 && e < E;
+  if (tid < kMaxE) cnt[tid] = 0;
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // the slots are taken kGroup chunks of 1024 at a time; a thread loads its
-  // ids of the whole group at once (one memory latency, not one per chunk)
-  const int nchunks = (TK + 1023) / 1024;
-  auto load_group = [&](int g0, int (&idv)[kGroup]) {
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      const int p = (g0 + k) * 1024 + tid;
-      idv[k] = (g0 + k < nchunks && p < TK) ? ids[p] : -1;
-    }
-    // wait for the loads here, in a form the compiler tracks: loads and stores
-    // share one counter, and without this the chunk loop would wait for its
-    // own scattered stores before every use of an id
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  };
-  // histogram: one LDS add per (wave, expert present in the wave's 64 slots)
-  for (int g0 = 0; g0 < nchunks; g0 += kGroup) {
-    int idv[kGroup];
-    load_group(g0, idv);
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      if (g0 + k >= nchunks) break;  // uniform
-      const int e = idv[k];
-      const bool valid = e >= 0 && e < E;
-      const uint64_t m = same_expert_lanes(e, valid);
-      if (valid && __popcll(m & lt_mask) == 0) atomicAdd(&cnt[e], __popcll(m));
-    }
-  }
+  const uint64_t m = same_expert_lanes(e, valid);
+  if (valid && __popcll(m & lt_mask) == 0) atomicAdd(&cnt[e], __popcll(m));
   __syncthreads();
-  if (tid < 64) scan_experts(cnt, E, base, offsets);
-  __syncthreads();
-  // stable scatter, 1024 slots at a time: a slot's position is its expert's
-  // running base, plus the counts of the earlier waves of the chunk, plus its
-  // rank among the equal slots of its wave
-  for (int g0 = 0; g0 < nchunks; g0 += kGroup) {
-    int idv[kGroup];
-    load_group(g0, idv);
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      if (g0 + k >= nchunks) break;  // uniform
-      const int p = (g0 + k) * 1024 + tid;
-      const int e = idv[k];
-      const bool valid = e >= 0 && e < E;
-      const uint64_t m = same_expert_lanes(e, valid);
-      const int rank = __popcll(m & lt_mask);
-      if (valid && rank == 0) wcnt[e][wave] = __popcll(m);
-      lds_barrier();
-      // one 16-lane row per expert: its waves' counts, scanned across the row
-      for (int i = tid; i < E * kWaves; i += 1024) {
-        const int x = i / kWaves, w = i % kWaves;
-        const int n = wcnt[x][w];
-        const int incl = row16_incl_scan(n);
-        const int b = base[x];
-        wpre[x][w] = b + incl - n;
-        wcnt[x][w] = 0;
-        if (w == kWaves - 1) base[x] = b + incl;
-      }
-      lds_barrier();
-      if (valid) {
-        const int pos = wpre[e][wave] + rank;
-        perm_src[pos] = p;
-        inv_pos[p] = pos;
-      } else if (p < TK) {
-        inv_pos[p] = -1;
+  for (int i = tid; i < E; i += kChunk) hist[size_t(c) * E + i] = cnt[i];
+}
+
+// Stable scatter of one chunk.  Every workgroup reduces the chunk counts
+// itself (the expert totals, and the counts of the chunks before its own), so
+// no workgroup waits for another; workgroup 0 also writes the offsets and the
+// tile list.  With a single chunk (hist NULL) the counts come from the chunk.
+__global__ __launch_bounds__(1024) void permute_scatter_kernel(const int* __restrict__ ids, int TK, int E,
+                                                               const int* __restrict__ hist, int nchunks,
+                                                               int* __restrict__ offsets, int* __restrict__ perm_src,
+                                                               int* __restrict__ inv_pos, int* tiles, int* ntiles,
+                                                               int bm) {
+  __shared__ int part[2][4][kMaxE];    // [before, total][quarter][expert]
+  __shared__ int tot[kMaxE];           // slots of each expert
+  __shared__ int first[kMaxE];         // position of this chunk's first slot of each expert
+  __shared__ int wcnt[kMaxE][kWaves];  // per (expert, wave): count, then first position
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = blockIdx.x;
+  const int p = c * kChunk + tid;
+  const int e = p < TK ? ids[p] : -1;
+  const bool valid = e >= 0 && e < E;
+  for (int i = tid; i < kMaxE * kWaves; i += kChunk) (&wcnt[0][0])[i] = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t m = same_expert_lanes(e, valid);
+  const int rank = __popcll(m & lt_mask);
+  if (hist) {
+    // thread (q, x) sums expert x over the chunks q, q + 4, ...
+    const int x = tid & (kMaxE - 1), q = tid >> 8;
+    int before = 0, total = 0;
+    if (x < E) {
+#pragma unroll 4
+      for (int cc = q; cc < nchunks; cc += 4) {
+        const int v = hist[size_t(cc) * E + x];
+        total += v;
+        before += cc < c ? v : 0;
       }
     }
+    part[0][q][x] = before;
+    part[1][q][x] = total;
+    __syncthreads();
+    if (tid < kMaxE) {
+      tot[tid] = part[1][0][tid] + part[1][1][tid] + part[1][2][tid] + part[1][3][tid];
+      first[tid] = part[0][0][tid] + part[0][1][tid] + part[0][2][tid] + part[0][3][tid];
+    }
+  } else {
+    if (tid < kMaxE) tot[tid] = first[tid] = 0;
+    __syncthreads();
+    if (valid && rank == 0) atomicAdd(&tot[e], __popcll(m));
   }
-  lds_barrier();
-  if (tiles) write_tiles(cnt, E, bm, tiles, ntiles, &wcnt[0][0]);
+  __syncthreads();
+  // expert offsets (exclusive scan of the totals) into part[0][0]
+  if (tid < 64) scan_experts(tot, E, &part[0][0][0], c == 0 ? offsets : nullptr);
+  if (valid && rank == 0) wcnt[e][wave] = __popcll(m);
+  __syncthreads();
+  // one 16-lane row per expert: the waves' counts, scanned across the row
+  for (int i = tid; i < E * kWaves; i += kChunk) {
+    const int x = i / kWaves;
+    const int n = wcnt[x][i % kWaves];
+    wcnt[x][i % kWaves] = part[0][0][x] + first[x] + row16_incl_scan(n) - n;
+  }
+  __syncthreads();
+  if (valid) {
+    const int pos = wcnt[e][wave] + rank;
+    perm_src[pos] = p;
+    inv_pos[p] = pos;
+  } else if (p < TK) {
+    inv_pos[p] = -1;
+  }
+  if (c == 0 && tiles) write_tiles(tot, E, bm, tiles, ntiles, &part[1][0][0]);
 }
 
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int* __restrict__ offsets, int E, int rows, int bm,
@@ -217,10 +212,16 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int* __restrict_
 
 }  // namespace
 
-hipError_t launch_permute(const int* ids, int TK, int E, int* offsets, int* perm_src, int* inv_pos, int* tiles,
-                          int* ntiles, int bm, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, TK, E, offsets, perm_src, inv_pos, tiles,
-                     ntiles, bm);
+hipError_t launch_permute(const int* ids, int TK, int E, int* hist, int* offsets, int* perm_src, int* inv_pos,
+                          int* tiles, int* ntiles, int bm, hipStream_t s) {
+  const int nchunks = (TK + kChunk - 1) / kChunk;
+  if (nchunks > 1) {
+    hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kChunk), 0, s, ids, TK, E, hist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kChunk), 0, s, ids, TK, E,
+                     nchunks > 1 ? hist : nullptr, nchunks, offsets, perm_src, inv_pos, tiles, ntiles, bm);
   return hipGetLastError();
 }
 
