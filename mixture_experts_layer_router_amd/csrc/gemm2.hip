@@ -4,24 +4,29 @@
 //   C[r][n] = sum_k A[r][k] * B_e[n][k]   for the rows r of expert e's segment
 //
 // Tile: 256 rows x 256 B rows, 64 bytes of K per step, 4 waves each owning
-// 128 x 128 (4 x 4 blocks of 32x32).  Measured on MI355X, a CU moves at most
-// about 64 bytes per clock from L2 into LDS or registers; this tile needs 32
-// bytes per clock at the full FP8 matrix rate (a 128 x 256 tile needs 47).
-// Four LDS stages of 32 KB, loaded four steps ahead with direct-to-LDS loads,
-// give three steps of memory latency slack.  Each lane keeps two register
-// sets of operands: the LDS reads of step s+1 and the loads of step s+4 are
-// issued among the MFMAs of step s in a fixed interleave.
+// 128 x 128 (4 x 4 blocks of 32x32).  Measured on MI355X, a CU moves about 64
+// bytes per clock from L2 into LDS when each load instruction covers whole
+// 128-byte row segments (8 rows x 128 B), but only about 32 when it covers
+// 16 rows x 64 B; this tile needs 32 bytes per clock at the full FP8 matrix
+// rate (a 128 x 256 tile needs 47).  So the loads move 128 bytes of each row,
+// two K steps, at a time: two LDS buffers of 64 KB (A and B, 256 rows x 128 B
+// each), double-buffered per step pair.  The loads of pair q+2 are issued
+// among the MFMAs of the odd step that starts pair q's second half, into the
+// buffer pair q has just released, and waited for two steps later.  Each lane
+// keeps two register sets of operands: the LDS reads of step s+1 go among
+// the MFMAs of step s.
 //
 //   bf16   v_mfma_f32_32x32x16_bf16, two per block per step
 //   MXFP8  v_mfma_scale_f32_32x32x64_f8f6f4, one per block per step, with the
 //          e8m0 scales of A and B per lane (lane l scales row l%32 for the
 //          32-deep K block l/32 of the instruction)
 //
-// LDS image: row r of a stage holds its 64 bytes as 4 chunks of 16, chunk c
-// at c ^ ((r >> 2) & 3), so the 16 lanes of one LDS read cycle (16 rows, one
-// chunk) hit 16 distinct bank groups.  Lane l's operand for a block is chunk
-// l/32 (bytes 0-15) and chunk 2 + l/32 (bytes 16-31) of row l%32: K bytes
-// [16g, 16g+16) and [32+16g, 48+16g), the instruction's K layout.
+// LDS image: row r of a buffer holds its 128 bytes (steps 2q, 2q+1) as 8
+// chunks of 16, chunk c at c ^ ((r >> 1) & 7), so the 16 lanes of one LDS
+// read cycle (16 rows, one chunk) hit 16 distinct bank groups.  Lane l's
+// operand for a block in step half h is chunk 4h + l/32 (bytes 0-15) and
+// chunk 4h + 2 + l/32 (bytes 16-31) of row l%32: K bytes [16g, 16g+16) and
+// [32+16g, 48+16g) of the step, the instruction's K layout.
 //
 // MX scales (one e8m0 byte per 32 K of a row) are loaded once per 8 steps
 // (512 K): 16 bytes per row per load, into one of three LDS buffers, so the
@@ -47,12 +52,13 @@ using namespace gemm_dev;
 constexpr int BM = kGemm2BM;  // 256 rows
 constexpr int BNT = 256;      // B rows per tile
 constexpr int BKB = 64;       // bytes of K per step
-constexpr int kStages = 4;
-constexpr int kLdsA = BM * BKB;   // 16 KB
-constexpr int kLdsB = BNT * BKB;  // 16 KB
+constexpr int RB = 2 * BKB;   // bytes per LDS row: a step pair
+constexpr int kBufs = 2;      // LDS buffers (step pairs)
+constexpr int kLdsA = BM * RB;    // 32 KB
+constexpr int kLdsB = BNT * RB;   // 32 KB
 constexpr int kSG = 8;            // K steps per MX scale group (512 K)
 constexpr int kSBuf = 3;          // MX scale group buffers
-constexpr int kDPS = 8;           // tile loads per wave per step
+constexpr int kDPP = 16;          // tile loads per wave per step pair
 
 struct Frag {
   i32x8 a[4];  // [32-row block i]: chunk g | chunk 2+g of the step's 64 bytes
@@ -63,7 +69,7 @@ struct Frag {
 template <int WF, int EPI>
 __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   constexpr bool MX = WF == W_MXFP8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * (kLdsA + kLdsB)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * (kLdsA + kLdsB)];
   __shared__ __attribute__((aligned(16))) uint8_t sS[MX ? kSBuf : 1][2][MX ? BM * 16 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -76,10 +82,11 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   if (!tl.valid) return;
   const int e = tl.e, m0 = tl.m0, n0 = tl.n0, seg0 = tl.seg0, mrows = tl.mrows, kz = tl.kz;
   const int K = p.K, N = p.N;
-  const int nk_all = K * esz<WF>() / BKB;
-  const int ks0 = int(long(nk_all) * kz / KS), ks1 = int(long(nk_all) * (kz + 1) / KS);
-  const int nk = ks1 - ks0;  // K steps of this slice, starting at step ks0
-  if (nk <= 0) return;
+  const int np_all = K * esz<WF>() / RB;
+  const int kp0 = int(long(np_all) * kz / KS), kp1 = int(long(np_all) * (kz + 1) / KS);
+  const int npair = kp1 - kp0;  // step pairs of this slice, starting at pair kp0
+  if (npair <= 0) return;
+  const int nk = 2 * npair;
   const uint32_t lda_b = uint32_t(p.lda) * esz<WF>();
   const uint32_t ldb_b = uint32_t(K) * esz<WF>();
 
@@ -89,27 +96,29 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
 #define PHYS_ROW(rl) uint32_t(a_map ? a_map[rbase + min((rl), rlast)] / a_div : rbase + min((rl), rlast))
 
   // ---------------------------------------------------------- load sources
-  // A: wave w loads tile rows [64w, 64w+64) as 4 blocks of 16; lane L fetches
-  // row 16k + L/4 of block k, chunk (L%4) ^ ((row>>2)&3).
+  // A: wave w loads tile rows [64w, 64w+64) as 8 blocks of 8; lane L fetches
+  // row 8k + L/8 of block k, chunk (L%8) ^ ((row>>1)&7).  Blocks wholly past
+  // the segment's rows are not loaded (their MFMA rows are never stored).
   const uint8_t* a_base = uniform_ptr(p.A);
-  uint32_t oa[4];
+  uint32_t oa[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = 64 * wave + 16 * k + (lane >> 2);
-    oa[k] = PHYS_ROW(r) * lda_b + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+  for (int k = 0; k < 8; ++k) {
+    const int r = 64 * wave + 8 * k + (lane >> 3);
+    oa[k] = PHYS_ROW(r) * lda_b + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
+  const int na_blk = min(max((mrows - 64 * wave + 7) / 8, 0), 8);
   // B: wave w loads tile B rows [64w, 64w+64); for EPI_GATEUP these are gate
   // rows (w even) or up rows (w odd) of intermediate columns n0 + 64 (w/2) + [0, 64)
   const uint8_t* b_base;
-  uint32_t ob[4];
+  uint32_t ob[8];
   {
     const void* bsrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1 : p.B0;
     b_base = uniform_ptr(static_cast<const uint8_t*>(bsrc) + size_t(e) * p.b_stride * esz<WF>());
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = 64 * wave + 16 * k + (lane >> 2);
-      const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + 16 * k + (lane >> 2) : min(n0 + t, N - 1);
-      ob[k] = uint32_t(br) * ldb_b + (((lane & 3) ^ ((t >> 2) & 3)) << 4);
+    for (int k = 0; k < 8; ++k) {
+      const int t = 64 * wave + 8 * k + (lane >> 3);
+      const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + 8 * k + (lane >> 3) : min(n0 + t, N - 1);
+      ob[k] = uint32_t(br) * ldb_b + (((lane & 7) ^ ((t >> 1) & 7)) << 4);
     }
   }
   // MX scales: wave w loads the 16 bytes of A rows and B rows [64w, 64w+64) of a group
@@ -126,13 +135,20 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   }
 #undef PHYS_ROW
 
-  const uint32_t lds_a0 = lds_addr(smem), lds_b0 = lds_a0 + kStages * kLdsA;
+  const uint32_t lds_a0 = lds_addr(smem), lds_b0 = lds_a0 + kBufs * kLdsA;
   const int ngroups = (nk + kSG - 1) / kSG;
-  auto tile_dma = [&](int d, int st, int kstep) {
-    if (d < 4)
-      dma16(oa[d], a_base + size_t(kstep) * BKB, lds_a0 + st * kLdsA + (64 * wave + 16 * d) * BKB);
-    else
-      dma16(ob[d - 4], b_base + size_t(kstep) * BKB, lds_b0 + st * kLdsB + (64 * wave + 16 * (d - 4)) * BKB);
+  // load d of pair q into buffer q % 2.  The steady-state waits drain every
+  // tile load, so loads past the last pair and of A blocks past the rows are
+  // skipped there; the prologue (full) issues all 16, clamped to the last
+  // pair, which keeps its wait count exact.
+  auto tile_dma = [&](int d, int q, bool full) {
+    if (!full && (q >= npair || (d < 8 && d >= na_blk))) return;
+    const int buf = q & 1, qq = min(q, npair - 1) + kp0;
+    if (d < 8) {
+      dma16(oa[d], a_base + size_t(qq) * RB, lds_a0 + buf * kLdsA + (64 * wave + 8 * d) * RB);
+    } else {
+      dma16(ob[d - 8], b_base + size_t(qq) * RB, lds_b0 + buf * kLdsB + (64 * wave + 8 * (d - 8)) * RB);
+    }
   };
   auto scale_dma = [&](int q) {  // scale group q (clamped) into buffer q % 3
     const int qq = min(q, ngroups - 1), buf = q % kSBuf;
@@ -140,26 +156,26 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
     dma16(obs, bs_base + 16 * qq, lds_addr(&sS[buf][1][64 * wave * 16]));
   };
 
-  // LDS operand reads: block i of the lane's rows, chunks g and 2+g
-  const int f = (l32 >> 2) & 3;
-  const int colo0 = (g ^ f) << 4, colo1 = ((2 + g) ^ f) << 4;
-  const int rowA = (128 * wm + l32) * BKB, rowB = (128 * wn + l32) * BKB;
+  // LDS operand reads: block i of the lane's rows, chunks 4h+g and 4h+2+g
+  const int f = (l32 >> 1) & 7;
+  const int rowA = (128 * wm + l32) * RB, rowB = (128 * wn + l32) * RB;
   const int srowA = (128 * wm + l32) * 16 + g, srowB = (128 * wn + l32) * 16 + g;
   constexpr int NR = 16 + (MX ? 8 : 0);  // LDS reads per step
   auto read_op = [&](int r, Frag& fr, int t) {  // read r of step t's operands
-    const int st = t % kStages;
-    const uint8_t* As_ = smem + st * kLdsA;
-    const uint8_t* Bs_ = smem + kStages * kLdsA + st * kLdsB;
+    const int buf = (t >> 1) & 1, h = t & 1;
+    const uint8_t* As_ = smem + buf * kLdsA;
+    const uint8_t* Bs_ = smem + kBufs * kLdsA + buf * kLdsB;
+    const int colo0 = ((4 * h + g) ^ f) << 4, colo1 = ((4 * h + 2 + g) ^ f) << 4;
     if (r < 8) {
       const int i = r / 2;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(As_ + rowA + 32 * BKB * i + ((r & 1) ? colo1 : colo0));
+      const i32x4 v = *reinterpret_cast<const i32x4*>(As_ + rowA + 32 * RB * i + ((r & 1) ? colo1 : colo0));
       if (r & 1)
         fr.a[i].hi = v;
       else
         fr.a[i].lo = v;
     } else if (r < 16) {
       const int j = (r - 8) / 2;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(Bs_ + rowB + 32 * BKB * j + ((r & 1) ? colo1 : colo0));
+      const i32x4 v = *reinterpret_cast<const i32x4*>(Bs_ + rowB + 32 * RB * j + ((r & 1) ? colo1 : colo0));
       if (r & 1)
         fr.b[j].hi = v;
       else
@@ -204,23 +220,25 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   };
 
   // step s: MFMAs on cur (read during step s-1) interleaved with the LDS reads
-  // of step s+1 into nxt and the loads of step s+4 into stage s % 4.  Past the
-  // last K step the loads repeat the last step into stages nothing reads again,
-  // so every step issues the same loads and the wait counts stay fixed.
-  auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t) {
-    wait_lgkm0();  // cur is in registers: this wave no longer reads stage s
-    // this wave's loads of step s+1 have landed: the loads of steps s-2 and s-1
-    // may still be in flight (8 each, plus 2 scale loads issued at steps = 0 mod 8)
-    const int sm = s & (kSG - 1);
-    if (MX && (sm == 1 || sm == 2))
-      wait_vm<2 * kDPS + 2>();
-    else
-      wait_vm<2 * kDPS>();
-    barrier();  // ... and every wave's; stage s % 4 is free for step s+4
-    if (MX && sm == 0) scale_dma(s / kSG + 1);
-    const int kd = min(s + kStages, nk - 1) + ks0, std_ = s % kStages;
+  // of step s+1 into nxt.  An odd step s = 2q+1 first waits for pair q+1 (read
+  // from step s on) and then, pair q's buffer being released by every wave,
+  // issues the loads of pair q+2 into it.  MX scale groups are loaded at the
+  // steps = 0 mod 8, two loads that may still be in flight at the next wait.
+  auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t, auto odd_t) {
+    constexpr bool odd = decltype(odd_t)::value;
+    wait_lgkm0();  // cur is in registers: this wave no longer reads step s's half
+    if constexpr (odd) {
+      if (MX && ((s - 1) & (kSG - 1)) == 0)
+        wait_vm<2>();
+      else
+        wait_vm<0>();
+      barrier();  // every wave's loads of pair q+1 have landed; pair q's buffer is free
+    } else {
+      if (MX && (s & (kSG - 1)) == 0) scale_dma(s / kSG + 1);
+    }
+    const int q2 = (s >> 1) + 2;
     // the reads go among the first half of the MFMAs, so they have landed
-    // when the next step starts; the loads go among the second half
+    // when the next step starts; the loads of an odd step go one per MFMA
     constexpr int NH = NM / 2;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -229,9 +247,10 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
       if (m < NH) {
 #pragma unroll
         for (int r = (m * NR) / NH; r < ((m + 1) * NR) / NH; ++r) read_op(r, nxt, s + 1);
-      } else {
+      }
+      if constexpr (odd) {
 #pragma unroll
-        for (int d = ((m - NH) * kDPS) / NH; d < ((m - NH + 1) * kDPS) / NH; ++d) tile_dma(d, std_, kd);
+        for (int d = (m * kDPP) / NM; d < ((m + 1) * kDPP) / NM; ++d) tile_dma(d, q2, false);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -241,23 +260,23 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   Frag f0, f1;
   if constexpr (MX) scale_dma(0);
 #pragma unroll
-  for (int t = 0; t < kStages; ++t)
+  for (int q = 0; q < kBufs; ++q)
 #pragma unroll
-    for (int d = 0; d < kDPS; ++d) tile_dma(d, t, min(t, nk - 1) + ks0);
-  wait_vm<(kStages - 1) * kDPS>();
+    for (int d = 0; d < kDPP; ++d) tile_dma(d, q, true);
+  wait_vm<kDPP>();  // pair 0 and scale group 0 (the loads of pair 1 may be in flight)
   barrier();
 #pragma unroll
   for (int r = 0; r < NR; ++r) read_op(r, f0, 0);
-  step(0, f0, f1, std::true_type{});
+  step(0, f0, f1, std::true_type{}, std::false_type{});
   int s = 1;
   for (; s + 1 < nk; s += 2) {
-    step(s, f1, f0, std::false_type{});
-    step(s + 1, f0, f1, std::false_type{});
+    step(s, f1, f0, std::false_type{}, std::true_type{});
+    step(s + 1, f0, f1, std::false_type{}, std::false_type{});
   }
-  if (s < nk) step(s, f1, f0, std::false_type{});
+  step(s, f1, f0, std::false_type{}, std::true_type{});  // nk is even: the last step is odd
   wait_vm<0>();
   wait_lgkm0();
-  barrier();  // the stages are free for the epilogue
+  barrier();  // the buffers are free for the epilogue
 
   // ------------------------------------------------------------ epilogue
   // lane l holds column l%32 of each 32x32 block, rows 8(r/4) + 4(l/32) + r%4
@@ -388,7 +407,7 @@ hipError_t launch_epi(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
 }  // namespace
 
 bool gemm2_serves(int wfmt, int K, int epi, int out_afmt, int ksplit) {
-  if (wfmt == W_BF16) return epi != EPI_GATEUP || out_afmt == A_NONE;
+  if (wfmt == W_BF16) return K % 64 == 0 && (epi != EPI_GATEUP || out_afmt == A_NONE);
   if (wfmt == W_MXFP8) return K % 512 == 0 && ksplit <= 1 && (epi != EPI_GATEUP || out_afmt != A_FP8_1X128);
   return false;
 }
