@@ -464,8 +464,8 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
   const bool gemv = fp == 1 || fp == 3 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
 
-  if (gemv && T <= kRouteGemvMaxT && fp != 3 && raf == A_NONE &&
-      (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt))) {
+  if (gemv && T <= kRouteGemvMaxT && fp != 3 && raf == A_NONE && size_t(T) * H * 2 <= size_t(kFusedXLdsMax) &&
+      H % 8 == 0 && (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt))) {
     // small T, bf16 activations: the whole layer in one persistent launch
     FusedDecodeParams fp_{};
     DecodeParams& dp = fp_.d;

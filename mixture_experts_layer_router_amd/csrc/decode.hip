@@ -50,9 +50,10 @@ namespace {
 constexpr int kQ = 32;         // queues, and most stripes of a counter
 constexpr int kLine = 32;      // words per 128-byte line
 constexpr int kUR = 2;         // intermediate columns per wave in a gate/up item
-constexpr int kURP = 1;        // ... computed per pass (2 * kURP weight rows in flight)
-constexpr int kUC = 3;         // weight chunks per row loaded together in a gate/up pass
+constexpr int kUC = 5;         // weight chunks per row loaded together (5 x 1024 covers H = 5120)
 constexpr int kUpCols = 4 * kUR;
+constexpr int kSUR = 2;        // ... in a shared gate/up item
+constexpr int kSUpCols = 4 * kSUR;
 constexpr int kDR = 4;         // output rows of a down item
 constexpr int kDJ = 3;         // down chunks per wave held in registers at once
 constexpr int kPhases = 3;     // phases that signal completion: R, SU, RG
@@ -60,8 +61,9 @@ constexpr uint64_t kWaitTicks = 20000000;  // s_memrealtime runs at 100 MHz: 0.2
 
 // Counter block (one counter per 128-byte line, word 0 of the line):
 //   line 0: error word                     lines 1..kQ: queue heads
-//   per phase f: item counter, ready flag
+//   per phase f: stripe summary, ready flag
 //   exit stripes (kQ) and exit summary
+//   per phase f: item counters of the kQ stripes
 struct Ctr {
   unsigned* base;
   MOE_DEV unsigned* error() const { return base; }
@@ -70,8 +72,9 @@ struct Ctr {
   MOE_DEV unsigned* flag(int f) const { return base + (2 + kQ + 2 * f) * kLine; }
   MOE_DEV unsigned* exit_stripe(int s) const { return base + (1 + kQ + 2 * kPhases + s) * kLine; }
   MOE_DEV unsigned* exit_summary() const { return exit_stripe(kQ); }
+  MOE_DEV unsigned* stripe(int f, int s) const { return base + (2 + 2 * kQ + 2 * kPhases + f * kQ + s) * kLine; }
 };
-constexpr int kCtrLines = 1 + kQ + 2 * kPhases + kQ + 1;
+constexpr int kCtrLines = 2 + 2 * kQ + 2 * kPhases + kPhases * kQ;
 static_assert(kCtrLines * kLine * 4 <= kFusedCtrBytes, "counter block");
 static_assert(kFusedErrorWord == 0, "error word");
 
@@ -88,13 +91,25 @@ MOE_DEV void store_agent(V* p, V v) {
 // clobber keeps the compiler from moving any store past it
 MOE_DEV void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Counts `cnt` finished items of phase f (of n).  Every thread calls it; the
-// workgroup's stores are complete before thread 0 counts the items.
-MOE_DEV void count_items(const Ctr& c, int f, int cnt, int n) {
+// Items i in [a, b) with i % kQ == q: the items of that range in queue q.
+MOE_DEV unsigned in_queue(int a, int b, int q) {
+  auto upto = [q](int x) { return x > q ? unsigned((x - q + kQ - 1) / kQ) : 0u; };
+  return upto(b) - upto(a);
+}
+
+// Counts `cnt` finished items of phase f, whose items are [a, b), run by a
+// workgroup of queue q.  A phase is counted in kQ stripes, one per queue (a
+// stripe's item count is known), so no counter takes more than the
+// increments of one queue's workgroups: same-address atomics serialise.  The
+// workgroup that completes a stripe counts it in the phase's summary, and
+// the one that completes the last stripe raises the flag.  Every thread calls
+// it; the workgroup's stores are complete before thread 0 counts the items.
+MOE_DEV void count_items(const Ctr& c, int f, int q, int cnt, int a, int b) {
   stores_done();
   __syncthreads();
   if (threadIdx.x == 0)
-    if (atomic_add(c.count(f), unsigned(cnt)) + unsigned(cnt) == unsigned(n)) store_agent(c.flag(f), 1u);
+    if (atomic_add(c.stripe(f, q), unsigned(cnt)) + unsigned(cnt) == in_queue(a, b, q))
+      if (atomic_inc(c.count(f)) + 1 == unsigned(min(b - a, kQ))) store_agent(c.flag(f), 1u);
 }
 
 // Bounded wait for phase f's ready flag; false if it gave up.
@@ -168,8 +183,101 @@ MOE_DEV void dn_math(const DnStage<WF>& st, const DownSrc& s, float (&acc)[kDR])
   }
 }
 
+// h[i0 .. i0+NR) = SiLU(x.Wg^T) * (x.Wu^T) for the token whose bf16 x row sits
+// in LDS as packed pairs (xl).  NC weight chunks of each of the 2 NR rows are
+// loaded together (at H = 5120 and NC = 5, a wave's whole item in one round
+// trip); x comes from LDS, so the registers hold only weights and scales.  h
+// is stored with agent-scope atomic stores (read by other workgroups inside
+// the launch once the phase is published).
+// a pointer the caller knows to be the same in every lane, in scalar registers
+MOE_DEV const uint8_t* uni(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v)));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v >> 32)));
+  return reinterpret_cast<const uint8_t*>((hi << 32) | lo);
+}
+
+template <int WF, int NR, int NC>
+MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u, const void* gs, const void* us,
+                         int i0, float* hrow) {
+  constexpr int CW = Fmt<WF>::CW, EPL = Fmt<WF>::EPL, ES = Fmt<WF>::ES;
+  constexpr int NS = WF == W_MXFP8 ? NR : 1;  // scales per chunk (FP8_B128: the rows share a 128-row block)
+  const int lane = lane_id();
+  // row bases are uniform (scalar registers); each lane adds a 32-bit offset
+  const uint8_t* gb[NR];
+  const uint8_t* ub[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    gb[r] = uni(static_cast<const uint8_t*>(g) + size_t(i0 + r) * H * ES);
+    ub[r] = uni(static_cast<const uint8_t*>(u) + size_t(i0 + r) * H * ES);
+  }
+  const uint8_t* gsb = nullptr;
+  const uint8_t* usb = nullptr;
+  if (WF == W_FP8_B128) {  // the 128-row block's scale row
+    gsb = uni(static_cast<const uint8_t*>(gs) + size_t(i0 >> 7) * (H >> 7) * 4);
+    usb = uni(static_cast<const uint8_t*>(us) + size_t(i0 >> 7) * (H >> 7) * 4);
+  }
+  float ag[NR] = {}, au[NR] = {};
+  const int kl = lane * EPL;
+  for (int k0 = 0; k0 < H; k0 += NC * CW) {
+    u32x4 wg[NC][NR], wu[NC][NR];
+    float sg[NC][NS], su[NC][NS];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c > 0 && k0 + c * CW >= H) break;  // uniform
+      const uint32_t k = uint32_t(min(k0 + c * CW + kl, H - EPL));
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        wg[c][r] = *reinterpret_cast<const u32x4*>(gb[r] + k * ES);
+        wu[c][r] = *reinterpret_cast<const u32x4*>(ub[r] + k * ES);
+      }
+      if (WF == W_FP8_B128) {
+        sg[c][0] = *reinterpret_cast<const float*>(gsb + (k >> 7) * 4);
+        su[c][0] = *reinterpret_cast<const float*>(usb + (k >> 7) * 4);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+          sg[c][r] = wscale<WF>(gs, i0 + r, int(k), H);
+          su[c][r] = wscale<WF>(us, i0 + r, int(k), H);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c > 0 && k0 + c * CW >= H) break;
+      const int kr = k0 + c * CW + kl;
+      const bool valid = kr < H;  // lanes past the row end add 0
+      const int k = min(kr, H - EPL);
+      uint32_t xp[EPL / 2];
+#pragma unroll
+      for (int i = 0; i < EPL / 8; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xl + k / 2 + 4 * i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xp[4 * i + q] = v[q];
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float sgr = valid ? sg[c][NS > 1 ? r : 0] : 0.0f;
+        const float sur = valid ? su[c][NS > 1 ? r : 0] : 0.0f;
+        ag[r] = fmaf(dot_chunk_bx<WF>(wg[c][r], xp), sgr, ag[r]);
+        au[r] = fmaf(dot_chunk_bx<WF>(wu[c][r], xp), sur, au[r]);
+      }
+    }
+  }
+  float mine = 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float gv = wave_sum(ag[r]);
+    const float uv = wave_sum(au[r]);
+    if (lane == r) mine = silu(gv) * uv;
+  }
+  if (lane < NR) __hip_atomic_store(hrow + i0 + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int WF>
-__global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) {
+__global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams p) {
+  // the T rows of x as bf16 pairs (T * H * 2 bytes of dynamic LDS)
+  extern __shared__ __attribute__((aligned(16))) uint32_t sx[];
   __shared__ float part[4][kRouteGemvMaxT];
   __shared__ float dpart[4][kDR];
   __shared__ int sids[kRouteGemvMaxT * 16];
@@ -180,7 +288,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) 
   const Ctr c{p.ctr};
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = d.T, H = d.H, K = d.rp.K, E = d.rp.E, I = p.I, Is = d.Is;
-  const int n[4] = {E, Is ? T * (Is / kUpCols) : 0, T * K * (I / kUpCols), T * (H / kDR)};
+  const int n[4] = {E, Is ? T * (Is / kSUpCols) : 0, T * K * (I / kUpCols), T * (H / kDR)};
   const int b1 = 0, b2 = b1 + n[1], b3 = b2 + n[2];  // queue items: SU, RG, DN (R is static)
   const unsigned total = unsigned(b3 + n[3]);
   const int q = blockIdx.x % kQ;
@@ -188,14 +296,17 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) 
   bool have_r = false, have_topk = false, have_dn_deps = false, poisoned = false;
   int pend_f = 0, pend_n = 0;  // finished items of phase pend_f not yet counted
   auto phase_of = [&](int i) { return i < b2 ? 1 : (i < b3 ? 2 : 3); };
+  for (int i = tid; i < T * H / 8; i += 256)
+    reinterpret_cast<u32x4*>(sx)[i] = reinterpret_cast<const u32x4*>(d.x)[i];
+  __syncthreads();
 
   // R: workgroup e < E computes router row e before it joins the queues (the
   // lowest block indices are dispatched first, so the routing, which every
   // routed item waits for, starts at once)
   if (int(blockIdx.x) < E) {
     if (tid == 0) s_next = q + kQ * atomic_inc(c.head(q));
-    router_row(d.x, T, d.wr, d.rp, blockIdx.x, d.logits, part, true);
-    count_items(c, 0, 1, E);
+    router_row(d.x, T, d.wr, d.rp, blockIdx.x, d.logits, part, true, sx);
+    count_items(c, 0, q, 1, 0, E);
   } else if (tid == 0) {
     s_next = q + kQ * atomic_inc(c.head(q));
   }
@@ -207,11 +318,9 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) 
     if (tid == 0) next = atomic_inc(c.head(q));
     const int it = int(item);
     if (it < b2) {  // SU: 8 shared intermediate columns of one token
-      const int i = it - b1, per = Is / kUpCols;
-      const int t = i / per, c0 = (i % per) * kUpCols + wave * kUR;
-#pragma unroll 1
-      for (int u = 0; u < kUR; u += kURP)
-        gate_up_item<WF, false, kURP, kUC, true>(d.x, H, t, d.sg, d.su, d.sgs, d.sus, c0 + u, d.hs + size_t(t) * Is);
+      const int i = it - b1, per = Is / kSUpCols;
+      const int t = i / per, c0 = (i % per) * kSUpCols + wave * kSUR;
+      gate_up_lds<WF, kSUR, kUC>(sx + size_t(t) * H / 2, H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is);
     } else {
       if (!have_topk) {  // every workgroup routes all T tokens itself (wave t: token t)
         if (!have_r) {
@@ -241,9 +350,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) 
         const uint8_t* ue = static_cast<const uint8_t*>(p.u) + e * ws;
         const uint8_t* gse = p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr;
         const uint8_t* use = p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr;
-#pragma unroll 1
-        for (int u = 0; u < kUR; u += kURP)
-          gate_up_item<WF, false, kURP, kUC, true>(d.x, H, slot / K, ge, ue, gse, use, c0 + u, p.h + size_t(slot) * I);
+        gate_up_lds<WF, kUR, kUC>(sx + size_t(slot / K) * H / 2, H, ge, ue, gse, use, c0, p.h + size_t(slot) * I);
       } else {  // DN: kDR output rows of one token over [shared Is | routed K*I]
         const int i = it - b3, nb = H / kDR;
         const int t = i / nb, n0 = (i % nb) * kDR;
@@ -311,7 +418,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) 
     item = s_next;
     __syncthreads();  // s_next is rewritten only after every thread has read it
     if (pend_n && (item >= total || phase_of(int(item)) != pend_f)) {  // end of a run: count it
-      count_items(c, pend_f, pend_n, n[pend_f]);
+      count_items(c, pend_f, q, pend_n, pend_f == 1 ? b1 : b2, pend_f == 1 ? b2 : b3);
       pend_n = 0;
     }
   }
@@ -330,22 +437,28 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedDecodeParams p) 
 
 template <int WF>
 hipError_t launch_fused(const FusedDecodeParams& p, hipStream_t s) {
-  // resident capacity of the device (more workgroups would only queue)
+  const size_t lds = size_t(p.d.T) * p.d.H * 2;
+  if (lds > size_t(kFusedXLdsMax) || p.d.H % 8) return hipErrorInvalidValue;
+  // resident capacity of the device for this LDS size (more workgroups would only queue)
   static int grid_for_dev[64] = {};
+  static size_t lds_for_dev[64] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int grid = dev < 64 ? grid_for_dev[dev] : 0;
+  int grid = dev < 64 && lds_for_dev[dev] == lds ? grid_for_dev[dev] : 0;
   if (grid == 0) {
     int per_cu = 0, cus = 0;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<WF>, 256, 0)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<WF>, 256, lds)) != hipSuccess)
       return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     grid = std::max(std::max(per_cu, 1) * cus, kQ);
-    if (dev < 64) grid_for_dev[dev] = grid;
+    if (dev < 64) {
+      grid_for_dev[dev] = grid;
+      lds_for_dev[dev] = lds;
+    }
   }
   grid = std::max(grid, p.d.rp.E);  // one workgroup per router row
-  hipLaunchKernelGGL((fused_decode_kernel<WF>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fused_decode_kernel<WF>), dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 

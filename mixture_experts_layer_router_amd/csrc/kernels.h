@@ -194,6 +194,7 @@ struct FusedDecodeParams {
 };
 constexpr int kFusedCtrBytes = 32768;
 constexpr int kFusedErrorWord = 0;  // ctr[0] != 0: a bounded wait gave up (never expected)
+constexpr int kFusedXLdsMax = 65536;  // bytes of x (T * H bf16) the launch stages in LDS
 hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ combine

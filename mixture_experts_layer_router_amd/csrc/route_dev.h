@@ -120,12 +120,39 @@ MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[
 // masked, so no load sits behind a branch); partial sums meet in `part` (LDS)
 // in wave order.  coherent: agent-scope atomic stores of the logits (read by
 // another workgroup in the same launch).
+// xl: when not null, x as bf16 pairs in LDS (token t's row at xl + t * H / 2),
+// read there instead of from x.
 MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* __restrict__ wr, const RouteParams& p,
-                        int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT], bool coherent = false) {
+                        int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT], bool coherent = false,
+                        const uint32_t* xl = nullptr) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint16_t* row = wr + size_t(e) * p.H;
   float acc[kRouteGemvMaxT] = {};
   // 256 threads x 8 bf16 = 2048 columns per pass; 4 passes issued together
+  if (xl) {
+    for (int k0 = 0; k0 < p.H; k0 += 4 * 2048) {
+      u32x4 wv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) wv[c] = *reinterpret_cast<const u32x4*>(row + min(k0 + c * 2048 + tid * 8, p.H - 8));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int k = min(k0 + c * 2048 + tid * 8, p.H - 8);
+        const float on = k0 + c * 2048 + tid * 8 < p.H ? 1.0f : 0.0f;
+#pragma unroll
+        for (int t = 0; t < kRouteGemvMaxT; ++t) {
+          if (t >= T) break;  // uniform
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + (size_t(t) * p.H + k) / 2);
+          float a = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(wv[c][q] << 16), a);
+            a = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[c][q] & 0xffff0000u), a);
+          }
+          acc[t] = fmaf(a, on, acc[t]);
+        }
+      }
+    }
+  } else
   for (int k0 = 0; k0 < p.H; k0 += 4 * 2048) {
     u32x4 wv[4], xv[4][kRouteGemvMaxT];
 #pragma unroll
