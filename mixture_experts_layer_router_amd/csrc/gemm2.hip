@@ -72,6 +72,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * (kLdsA + kLdsB)];
   __shared__ __attribute__((aligned(16))) uint8_t sS[MX ? kSBuf : 1][2][MX ? BM * 16 : 16];
 
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -223,12 +224,16 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   // of step s+1 into nxt.  An odd step s = 2q+1 first waits for pair q+1 (read
   // from step s on) and then, pair q's buffer being released by every wave,
   // issues the loads of pair q+2 into it.  MX scale groups are loaded at the
-  // steps = 0 mod 8, two loads that may still be in flight at the next wait.
-  auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t, auto odd_t) {
+  // steps = 0 mod 8.  Loads complete in issue order, so the wait leaves out
+  // exactly the scale loads issued at step s-1 (at step 1, the step-1 case
+  // is peeled at compile time).
+  auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t, auto odd_t, auto step1_t) {
     constexpr bool odd = decltype(odd_t)::value;
     wait_lgkm0();  // cur is in registers: this wave no longer reads step s's half
     if constexpr (odd) {
-      if (MX && ((s - 1) & (kSG - 1)) == 0)
+      if constexpr (decltype(step1_t)::value)
+        wait_vm<MX ? 2 : 0>();
+      else if (MX && ((s - 1) & (kSG - 1)) == 0)
         wait_vm<2>();
       else
         wait_vm<0>();
@@ -267,13 +272,14 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   barrier();
 #pragma unroll
   for (int r = 0; r < NR; ++r) read_op(r, f0, 0);
-  step(0, f0, f1, std::true_type{}, std::false_type{});
-  int s = 1;
-  for (; s + 1 < nk; s += 2) {
-    step(s, f1, f0, std::false_type{}, std::true_type{});
-    step(s + 1, f0, f1, std::false_type{}, std::false_type{});
+  const std::false_type no{};
+  const std::true_type yes{};
+  step(0, f0, f1, yes, no, no);
+  step(1, f1, f0, no, yes, yes);  // nk >= 2
+  for (int s = 2; s + 1 < nk; s += 2) {  // nk is even: steps come in (even, odd) pairs
+    step(s, f0, f1, no, no, no);
+    step(s + 1, f1, f0, no, yes, no);
   }
-  step(s, f1, f0, std::false_type{}, std::true_type{});  // nk is even: the last step is odd
   wait_vm<0>();
   wait_lgkm0();
   barrier();  // the buffers are free for the epilogue
