@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--replicas", type=int, default=24)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 2048-token workload")
+    ap.add_argument("--no-small-m", action="store_true", help="skip the 2-8 token DeepSeek-V2 layers")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--secondary-only", action="store_true",
                     help="only run the 2048-token workload (for profiling its kernels)")
@@ -205,6 +206,8 @@ def main():
 
     if not args.no_secondary:
         out["secondary"] = secondary(args, moe, synth, torch)
+    if not args.no_small_m:
+        out["small_m"] = small_m(moe, synth, torch)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, reps[0], layers[0], torch)
@@ -244,6 +247,32 @@ def measured_traffic(kernel):
     if fields.get("sources sha256 at measurement") != csrc_hash(kernel) or "traffic_bytes" not in fields:
         return None
     return int(fields["traffic_bytes"])
+
+
+def small_m(moe, synth, torch, tokens=(2, 4, 8), replicas=8):
+    """The DeepSeek-V2 layer at a few tokens (verify-sized batches): us/layer
+    and the HBM rate of the bytes the routing touches, 8 replicas cycled."""
+    base = synth.get_config("dsv2_b1")
+    res = []
+    for T in tokens:
+        cfg = base.derive(tokens=T)
+        reps = [synth.make_inputs(cfg, "cuda:0", replica=r) for r in range(replicas)]
+        layers = [moe.Layer(cfg, inp) for inp in reps]
+        ms, _ = time_layers(layers, [inp.x for inp in reps], 100, 10, torch)
+        nbytes = []
+        for lay, inp in zip(layers, reps):
+            _, ids, _ = lay.forward()
+            torch.cuda.synchronize()
+            touched = sorted(set(ids.flatten().tolist()))
+            nbytes.append(wbytes(inp.routed, touched) + wbytes(inp.shared, [0]) + inp.w_router.numel() * 2 +
+                          inp.x.numel() * 2 * 2)
+        b = statistics.mean(nbytes)
+        res.append({"tokens": T, "us_per_layer": round(ms * 1e3, 2), "algorithmic_bytes": int(b),
+                    "hbm_GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                    "path": "single launch" if T <= 4 else "staged GEMV launches"})
+        del layers, reps
+        torch.cuda.empty_cache()
+    return res
 
 
 def secondary(args, moe, synth, torch):
