@@ -232,9 +232,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   // MFMA m of a step (bf16 / MXFP8): K part outermost, so the two MFMAs on one
   // accumulator are NI*4 instructions apart.  In the first step the first
   // MFMA of each accumulator starts from zero (no zero-filled registers).
+  // B blocks of this wave that hold columns below N (the others are not computed)
+  const int nJ = EPI == EPI_GATEUP ? 4 : min(max((N - n0 - 128 * wn + 31) / 32, 0), 4);
   auto mfma_op = [&](int m, const Frag& f, auto ni_t, auto first_t) {
     constexpr int NI = decltype(ni_t)::value;
     const int kq = m / (NI * 4), i = (m / 4) % NI, j = m % 4;
+    if (j >= nJ) return;
     f32x16 c = acc[i][j];
     if (decltype(first_t)::value && kq == 0) {
 #pragma unroll

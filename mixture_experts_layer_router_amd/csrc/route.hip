@@ -24,6 +24,33 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
   router_row(x, T, wr, p, blockIdx.x, logits, part);
 }
 
+// topk_load for logits summed over nslice split-K slices: every slice value
+// of the lane's experts is loaded before any is added (one memory latency, not
+// one per slice), then the slices are added in slice order as topk_load does.
+MOE_DEV void topk_load_sliced(const RouteParams& p, const TopkLayout& L, const float* logits_row, const float* bias,
+                              float (&lg)[kMpl], int nslice, long slice_stride) {
+  float s[kMpl][kRouterMaxSplit];
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) {
+    const int e = L.expert(p, j);
+#pragma unroll
+    for (int z = 0; z < kRouterMaxSplit; ++z) s[j][z] = (e >= 0 && z < nslice) ? logits_row[z * slice_stride + e] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) {
+    const int e = L.expert(p, j);
+    float v = kNegInfF;
+    if (e >= 0) {
+      v = s[j][0];
+#pragma unroll
+      for (int z = 1; z < kRouterMaxSplit; ++z)
+        if (z < nslice) v += s[j][z];
+      if (bias) v += bias[e];
+    }
+    lg[j] = v;
+  }
+}
+
 // One wave per token over fp32 logits [T][E] (bias added here).
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T,
                                                    const float* __restrict__ bias, RouteParams p, int* ids,
@@ -32,7 +59,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;  // whole wave
   const TopkLayout L(p, lane_id());
   float lg[kMpl];
-  topk_load(p, L, logits + size_t(t) * p.E, bias, lg, nslice, slice_stride);
+  if (nslice > 1)
+    topk_load_sliced(p, L, logits + size_t(t) * p.E, bias, lg, nslice, slice_stride);
+  else
+    topk_load(p, L, logits + size_t(t) * p.E, bias, lg);
   topk_select(p, L, lg, ids + size_t(t) * p.K, w + size_t(t) * p.K);
 }
 
