@@ -130,7 +130,10 @@ def test_route(name):
 # ---------------------------------------------------------------- dispatch
 
 @pytest.mark.parametrize("afmt", ["none", "fp8_1x128", "mxfp8_1x32"])
-@pytest.mark.parametrize("T,E,K", [(1, 160, 6), (500, 160, 6), (333, 7, 3), (64, 256, 8)])
+# slots T*K: 6; 3,000 (3 chunks of 1,024); 999; 512; exactly 1,024 (one full chunk); 2,049 (a
+# 1-slot tail chunk); 24,576 (24 chunks, skewed like the 4,096-token workload)
+@pytest.mark.parametrize("T,E,K", [(1, 160, 6), (500, 160, 6), (333, 7, 3), (64, 256, 8), (512, 16, 2),
+                                   (683, 12, 3), (4096, 160, 6)])
 def test_permute(T, E, K, afmt):
     rng = np.random.default_rng(T * 7 + E + K)
     if E == 160 and T > 1:   # skewed popularity, leaves some experts empty
