@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 2048-token workload")
     ap.add_argument("--no-small-m", action="store_true", help="skip the 2-8 token DeepSeek-V2 layers")
+    ap.add_argument("--no-batched", action="store_true", help="skip the 256- and 4096-token DeepSeek-V2 layers")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--secondary-only", action="store_true",
                     help="only run the 2048-token workload (for profiling its kernels)")
@@ -208,6 +209,8 @@ def main():
         out["secondary"] = secondary(args, moe, synth, torch)
     if not args.no_small_m:
         out["small_m"] = small_m(moe, synth, torch)
+    if not args.no_batched:
+        out["batched"] = batched(moe, synth, torch)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, reps[0], layers[0], torch)
@@ -247,6 +250,38 @@ def measured_traffic(kernel):
     if fields.get("sources sha256 at measurement") != csrc_hash(kernel) or "traffic_bytes" not in fields:
         return None
     return int(fields["traffic_bytes"])
+
+
+def batched(moe, synth, torch, steps=20):
+    """The DeepSeek-V2 FP8 layer at 256 tokens (near-uniform routing) and at
+    4,096 tokens (Zipf-skewed routing): us/layer, the HBM rate of the bytes
+    the routing touches (weights of the touched experts, shared expert,
+    router, x and out) and the matrix rate of the flops over real rows.
+    Both working sets exceed the 256 MB memory-side cache."""
+    res = []
+    for name in ("dsv2_256tok", "dsv2_4096tok_zipf"):
+        cfg = synth.get_config(name)
+        inp = synth.make_inputs(cfg, "cuda:0")
+        lay = moe.Layer(cfg, inp)
+        ms, _ = time_layers([lay], [inp.x], steps, 3, torch)
+        _, ids, _ = lay.forward()
+        torch.cuda.synchronize()
+        touched = sorted(set(ids.flatten().tolist()))
+        T, H, K, I, Is, E = cfg.tokens, cfg.hidden, cfg.topk, cfg.inter, cfg.shared_inter, cfg.n_experts
+        nbytes = (wbytes(inp.routed, touched) + wbytes(inp.shared, [0]) + inp.w_router.numel() * 2 +
+                  inp.x.numel() * 2 * 2)
+        flops = 2.0 * T * K * 3 * H * I + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
+        kern = trace_kernels([lay], [inp.x], 3, moe, torch)
+        res.append({"workload": name, "tokens": T, "us_per_layer": round(ms * 1e3, 2),
+                    "touched_experts": len(touched), "algorithmic_bytes": int(nbytes),
+                    "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "frac_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                    "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in kern.items()}})
+        del lay, inp
+        torch.cuda.empty_cache()
+    return res
 
 
 def small_m(moe, synth, torch, tokens=(2, 4, 8), replicas=8):
