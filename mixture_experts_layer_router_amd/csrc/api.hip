@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -162,6 +163,40 @@ struct Trace {
   const char* names[128] = {};
 } g_trace;
 
+// Second stream of the batched path, per device, for a shared expert too
+// small to fill the chip: its FFN needs only x, so it runs beside the routing,
+// dispatch and routed experts and joins back before the combine.  Created on
+// first use (default priority, non-blocking); the mutex keeps each call's
+// fork and join enqueues together when several host threads call in.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+// the side stream of the current device, or null if it cannot be had
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(s);
+      return nullptr;
+    }
+    ss.fork = f;
+    ss.join = j;
+    ss.s = s;
+  }
+  return &ss;
+}
+
 template <class F>
 hipError_t traced(const char* name, hipStream_t s, F&& f) {
   if (!g_trace.ev || 2 * g_trace.n + 1 >= g_trace.max || g_trace.n >= 128) return f();
@@ -258,6 +293,27 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   d.ldc = H;
   LAUNCH(routed ? "gemm_down_routed" : "gemm_down_shared", launch_gemm(wf, y_bf16 ? EPI_BF16 : EPI_F32, d, s));
   return MOE_OK;
+}
+
+// The batched shared FFN on all T rows of x, on stream s, using only its own
+// workspace regions (x quantised into xs2 in the shared activation format,
+// h in hsh, y in ysh); *ysh gets the fp32 output rows.
+moe_status shared_ffn(const moe_config* cfg, const uint16_t* x, int T, const moe_ffn_weights* shared, void* ws,
+                      const Ws& L, float** ysh, hipStream_t s) {
+  hipStream_t s_ = s;
+  const int H = cfg->hidden, saf = cfg->shared_afmt;
+  const void* xs = x;
+  const void* xss = nullptr;
+  if (saf != A_NONE) {
+    LAUNCH("quant_rows_shared", launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2),
+                                                  at<void>(ws, L.xs2s), nullptr, s));
+    xs = at<void>(ws, L.xs2);
+    xss = at<void>(ws, L.xs2s);
+  }
+  *ysh = at<float>(ws, L.ysh);
+  return gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
+                  ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
+                  at<void>(ws, L.hshs), *ysh, false, s);
 }
 
 }  // namespace
@@ -576,6 +632,26 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
     return MOE_OK;
   }
 
+  // batched path, shared expert whose gate/up grid fills at most half the
+  // CUs (128-row tiles, 128 output columns each): it forks onto the side
+  // stream before the routing.  A larger one stays in order on the caller's
+  // stream: beside the routed GEMMs it measured slower (their tiles take the
+  // same CUs).
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  float* ysh = nullptr;
+  if (!gemv && has_shared &&
+      long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128) {
+    side_lock.lock();
+    side = side_stream();
+    if (side) {
+      HIP_TRY(hipEventRecord(side->fork, stream));
+      HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
+      if ((st = shared_ffn(cfg, x, T, shared, ws, L, &ysh, side->s)) != MOE_OK) return st;
+      HIP_TRY(hipEventRecord(side->join, side->s));
+    }
+  }
+
   if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
 
   if (gemv) {  // T > kRouteGemvMaxT on the GEMV path: routed + shared gate/up in one launch
@@ -662,8 +738,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, rbm), rbm, routed,
                      at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
     return st;
-  float* ysh = nullptr;
-  if (has_shared) {
+  if (has_shared && !side) {  // in order on the caller's stream
     const void* xs = x;
     const void* xss = nullptr;
     if (saf != A_NONE) {
@@ -683,6 +758,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
                        at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
       return st;
   }
+  if (side) HIP_TRY(hipStreamWaitEvent(stream, side->join, 0));
   LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
   return MOE_OK;
 }
