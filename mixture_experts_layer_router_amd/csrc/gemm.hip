@@ -26,11 +26,12 @@
 // [16g, 16g+16) and [32+16g, 48+16g) of the half, g = l/32), a bf16
 // instruction for K quarter q takes slot q.
 //
-// bf16 and MXFP8 keep two register sets of operands: the reads of step s+1
-// are issued among the MFMAs of step s, together with the direct-to-LDS loads
-// of step s+3, in a fixed interleave, so the matrix pipe does not wait for LDS
-// at the step boundary.  FP8_B128 needs the registers for its temporaries and
-// reads each step's operands at the start of the step.
+// bf16, MXFP8 and the FP8_B128 gate/up keep two register sets of operands:
+// the reads of step s+1 are issued among the MFMAs of step s, together with
+// the direct-to-LDS loads of step s+3, in a fixed interleave, so the matrix
+// pipe does not wait for LDS at the step boundary.  The FP8_B128 down GEMMs
+// need those registers for their temporaries beside their epilogue and read
+// each step's operands at the start of the step.
 //
 // Rows come from a device tile list written by the dispatch kernel, so no
 // expert count is read back to the host (Mixture-of-Kittens, Abstract); the
@@ -74,6 +75,7 @@ struct Frag {
   i32x8 a[2][2];  // [32-row block i][K half]
   i32x8 b[4][2];  // [32-row B block j][K half]
   uint32_t sa[2], sb[4];  // MXFP8: the four e8m0 scales of the step, one byte per K block
+  f32x4 fa[2][4];         // FP8_B128: activation scales of the lane's 16 rows per block i
 };
 MOE_DEV void set_slot(i32x8& v, int c, i32x4 x) {
   if (c & 1)
@@ -255,7 +257,97 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
   // ------------------------------------------------------------ main loop
   const bool two = 64 * wm + 32 < mrows;  // this wave's second row block holds valid rows
-  if constexpr (WF == W_FP8_B128) {
+  if constexpr (WF == W_FP8_B128 && EPI == EPI_GATEUP) {
+    // Pipelined like the other formats: the operands and activation scales
+    // of step s+1 are read among the MFMAs of step s, the loads of step s+3
+    // issued among them too.  One 128-byte step is one 128-deep scale block:
+    // per half jh of the B blocks, the first K half of every (i, j) block
+    // goes into a temporary, the second accumulates onto it, and the
+    // temporaries are promoted into acc with the activation scale of each
+    // row times the weight scale of the wave's B rows.
+    auto run = [&](auto ni_t) {
+      constexpr int NI = decltype(ni_t)::value;
+      constexpr int NM = NI * 8;                // MFMAs per step: two per (i, j) block
+      constexpr int NR = NI * 4 + 16 + NI * 4;  // LDS reads: A slots, B slots, activation scale vectors
+      auto read_b128 = [&](int r, Frag& f, int st) {
+        if (r < NI * 4 + 16) {
+          read_op(r, f, st, ni_t);
+        } else {
+          const int v = r - NI * 4 - 16, i = v / 4, q = v % 4;
+          f.fa[i][q] = *reinterpret_cast<const f32x4*>(&sAS[st][64 * wm + 32 * i + 8 * q + 4 * g]);
+        }
+      };
+      auto step = [&](int s, Frag& cur, Frag& nxt) {
+        wait_lgkm0();    // cur is in registers: this wave no longer reads stage s
+        wait_vm<DPS>();  // this wave's loads of step s+1 have landed
+        barrier();       // ... and every wave's; stage s % 3 is free for step s+3
+        const int stn = (s + 1) % kStages, std_ = s % kStages;
+        const int kd = min(s + 3, nk - 1) + ks0;
+        const float w0 = sWs[wave][0][s + ks0], w1 = sWs[wave][1][s + ks0];
+        f32x16 t[2][2];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const int jh = m / (NI * 4), hf = (m / (NI * 2)) % 2, blk = m % (NI * 2);
+          const int i = blk / 2, jj = blk % 2, j = 2 * jh + jj;
+          if (j < nJ) {
+            if (hf == 0) {
+              f32x16 z;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) z[r] = 0.f;
+              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i][0], cur.b[j][0], z, 0, 0, 0, 127, 0,
+                                                                         127);
+            } else {
+              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i][1], cur.b[j][1], t[i][jj], 0, 0, 0,
+                                                                         127, 0, 127);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = (m * NR) / NM; r < ((m + 1) * NR) / NM; ++r) read_b128(r, nxt, stn);
+#pragma unroll
+          for (int d = (m * DPS) / NM; d < ((m + 1) * DPS) / NM; ++d) dma_op(d, std_, kd);
+          __builtin_amdgcn_sched_barrier(0);
+          if (hf == 1 && blk == NI * 2 - 1) {  // the half's temporaries are complete: promote them
+            const float wj = (EPI == EPI_GATEUP && jh == 1) ? w1 : w0;
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+              for (int j2 = 0; j2 < 2; ++j2) {
+                const int jo = 2 * jh + j2;
+                if (jo < nJ) {
+#pragma unroll
+                  for (int r = 0; r < 16; ++r)
+                    acc[ii][jo][r] = fmaf(t[ii][j2][r], cur.fa[ii][r / 4][r % 4] * wj, acc[ii][jo][r]);
+                }
+              }
+          }
+        }
+      };
+      Frag f0, f1;
+      issue(0);
+      issue(min(1, nk - 1));
+      issue(min(2, nk - 1));
+      wait_vm<2 * DPS>();
+      barrier();
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_b128(r, f0, 0);
+      step(0, f0, f1);
+      int s = 1;
+      for (; s + 1 < nk; s += 2) {
+        step(s, f1, f0);
+        step(s + 1, f0, f1);
+      }
+      if (s < nk) step(s, f1, f0);
+    };
+    if (nk > 0) {
+      if (two)
+        run(IC<2>{});
+      else
+        run(IC<1>{});
+    }
+  } else if constexpr (WF == W_FP8_B128) {
+    // the down GEMMs: the pipelined form's registers do not fit beside their
+    // epilogue, so each step reads its operands when it starts
     auto run = [&](auto ni_t) {
       constexpr int NI = decltype(ni_t)::value;
       if (nk > 0) issue(0);
