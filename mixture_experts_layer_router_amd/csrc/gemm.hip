@@ -257,7 +257,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
   // ------------------------------------------------------------ main loop
   const bool two = 64 * wm + 32 < mrows;  // this wave's second row block holds valid rows
-  if constexpr (WF == W_FP8_B128 && EPI == EPI_GATEUP) {
+  // the down GEMMs' epilogues leave the pipelined form too few registers
+  constexpr bool B128_PIPE = EPI == EPI_GATEUP;
+  if constexpr (WF == W_FP8_B128 && B128_PIPE) {
     // Pipelined like the other formats: the operands and activation scales
     // of step s+1 are read among the MFMAs of step s, the loads of step s+3
     // issued among them too.  One 128-byte step is one 128-deep scale block:
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         for (int m = 0; m < NM; ++m) {
           const int jh = m / (NI * 4), hf = (m / (NI * 2)) % 2, blk = m % (NI * 2);
           const int i = blk / 2, jj = blk % 2, j = 2 * jh + jj;
-          if (j < nJ) {
+          {  // every B block (B rows past N are clamped loads; their columns are not stored)
             if (hf == 0) {
               f32x16 z;
 #pragma unroll
@@ -314,11 +316,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
               for (int j2 = 0; j2 < 2; ++j2) {
                 const int jo = 2 * jh + j2;
-                if (jo < nJ) {
 #pragma unroll
-                  for (int r = 0; r < 16; ++r)
-                    acc[ii][jo][r] = fmaf(t[ii][j2][r], cur.fa[ii][r / 4][r % 4] * wj, acc[ii][jo][r]);
-                }
+                for (int r = 0; r < 16; ++r)
+                  acc[ii][jo][r] = fmaf(t[ii][j2][r], cur.fa[ii][r / 4][r % 4] * wj, acc[ii][jo][r]);
               }
           }
         }
