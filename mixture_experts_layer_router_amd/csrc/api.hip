@@ -175,24 +175,29 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[64];
 
-// the side stream of the current device, or null if it cannot be had
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+// the side stream of the device that `caller` runs on, or null if it cannot be had
+SideStream* side_stream(hipStream_t caller) {
+  int dev = 0, cur = 0;
+  if (hipStreamGetDevice(caller, &dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   SideStream& ss = g_side[dev];
   if (!ss.s) {
+    if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(dev) != hipSuccess) return nullptr;
     hipStream_t s = nullptr;
     hipEvent_t f = nullptr, j = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&j, hipEventDisableTiming) == hipSuccess;
+    if (ok) {
+      ss.fork = f;
+      ss.join = j;
+      ss.s = s;
+    } else {
+      if (j) (void)hipEventDestroy(j);
       if (f) (void)hipEventDestroy(f);
-      (void)hipStreamDestroy(s);
-      return nullptr;
+      if (s) (void)hipStreamDestroy(s);
     }
-    ss.fork = f;
-    ss.join = j;
-    ss.s = s;
+    (void)hipSetDevice(cur);
+    if (!ok) return nullptr;
   }
   return &ss;
 }
@@ -643,7 +648,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   if (!gemv && has_shared &&
       long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128) {
     side_lock.lock();
-    side = side_stream();
+    side = side_stream(stream);
     if (side) {
       HIP_TRY(hipEventRecord(side->fork, stream));
       HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
