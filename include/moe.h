@@ -28,8 +28,9 @@
  * - The caller owns all memory.  The library never allocates.  Calls that
  *   take a workspace need `ws_bytes` >= moe_workspace_size(); the workspace
  *   must be zero-filled once before its first use (torch.zeros is enough):
- *   its first 32 KiB hold the work queues and counters of moe_forward's
- *   single-launch path, which every call leaves zero again.  Calls sharing
+ *   its first 32 KiB hold the work queues, counters, a launch epoch and
+ *   tagged router logits of moe_forward's single-launch path; every call
+ *   leaves the queues and counters zero again and advances the epoch.  Calls sharing
  *   one workspace must be ordered on one stream; overlapping calls on one
  *   workspace race.
  * - Status codes: nothing is thrown across the ABI.  Host-side validation

@@ -6,8 +6,14 @@
 //
 // Router rows come first: workgroup e < E computes row e of the logits
 // (all tokens) as soon as it starts; the lowest block indices are dispatched
-// first, and the routing is what every routed item waits for.  The rest of
-// the work is a list of items in dependency order:
+// first, and the routing is what every routed item waits for.  The logits
+// are handed over tagged: each is a 64-bit word holding the launch's tag
+// (from an epoch word that the last workgroup out advances) beside the float,
+// and a workgroup that needs the routing polls the E words of each token
+// until all carry this launch's tag.  That costs one round trip after the
+// last router row, where counting the rows and raising a flag would cost
+// three (two atomics and the flag read) on a memory system busy with weight
+// streams.  The rest of the work is a list of items in dependency order:
 //   SU  shared gate/up         (8 intermediate columns of one token)
 //   RG  routed gate/up         (8 intermediate columns of one (token, slot))
 //   DN  down + combine         (4 output rows of one token: the shared and
@@ -56,17 +62,20 @@ constexpr int kSUR = 2;        // ... in a shared gate/up item
 constexpr int kSUpCols = 4 * kSUR;
 constexpr int kDR = 4;         // output rows of a down item
 constexpr int kDJ = 3;         // down chunks per wave held in registers at once
-constexpr int kPhases = 3;     // phases that signal completion: R, SU, RG
+constexpr int kPhases = 2;     // phases that signal completion: SU, RG
 constexpr uint64_t kWaitTicks = 20000000;  // s_memrealtime runs at 100 MHz: 0.2 s
 
 // Counter block (one counter per 128-byte line, word 0 of the line):
-//   line 0: error word                     lines 1..kQ: queue heads
+//   line 0: error word, epoch word         lines 1..kQ: queue heads
 //   per phase f: stripe summary, ready flag
 //   exit stripes (kQ) and exit summary
 //   per phase f: item counters of the kQ stripes
 struct Ctr {
   unsigned* base;
   MOE_DEV unsigned* error() const { return base; }
+  MOE_DEV unsigned* epoch() const { return base + kFusedEpochWord; }
+  // tagged router logits [T][E] (64-bit words, past the counter lines)
+  MOE_DEV uint64_t* tagged() const { return reinterpret_cast<uint64_t*>(base + kFusedTagOff / 4); }
   MOE_DEV unsigned* head(int q) const { return base + (1 + q) * kLine; }
   MOE_DEV unsigned* count(int f) const { return base + (1 + kQ + 2 * f) * kLine; }
   MOE_DEV unsigned* flag(int f) const { return base + (2 + kQ + 2 * f) * kLine; }
@@ -75,8 +84,9 @@ struct Ctr {
   MOE_DEV unsigned* stripe(int f, int s) const { return base + (2 + 2 * kQ + 2 * kPhases + f * kQ + s) * kLine; }
 };
 constexpr int kCtrLines = 2 + 2 * kQ + 2 * kPhases + kPhases * kQ;
-static_assert(kCtrLines * kLine * 4 <= kFusedCtrBytes, "counter block");
-static_assert(kFusedErrorWord == 0, "error word");
+static_assert(kCtrLines * kLine * 4 <= kFusedTagOff, "counter lines");
+static_assert(kFusedTagOff + kRouteGemvMaxT * 256 * 8 <= kFusedCtrBytes, "tagged logits");
+static_assert(kFusedErrorWord == 0 && kFusedEpochWord < kLine, "line 0 words");
 
 MOE_DEV unsigned atomic_add(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -131,6 +141,48 @@ MOE_DEV bool wait_flag(const Ctr& c, int f, int* s_ok) {
   }
   __syncthreads();
   return *s_ok != 0;
+}
+
+// One wave: token row `row` of the tagged logits into the top-k layout
+// (+ bias), once every expert's word carries `tag`.  Bounded like wait_flag;
+// false (and the error word set) if it gave up.  Agent-scope loads: a line
+// this XCD's L2 held from before the producer's store would show an old tag.
+MOE_DEV bool load_tagged_logits(const RouteParams& rp, const TopkLayout& L, const uint64_t* row, const float* bias,
+                                unsigned tag, float (&lg)[kMpl], unsigned* err) {
+  uint64_t v[kMpl];
+  bool mine = true;
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) {
+    const int e = L.expert(rp, j);
+    v[j] = e >= 0 ? __hip_atomic_load(row + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    mine &= e < 0 || unsigned(v[j] >> 32) == tag;
+  }
+  bool ok = true;
+  if (!__all(mine)) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    do {
+      __builtin_amdgcn_s_sleep(1);
+      mine = true;
+#pragma unroll
+      for (int j = 0; j < kMpl; ++j) {
+        const int e = L.expert(rp, j);
+        if (e >= 0 && unsigned(v[j] >> 32) != tag)
+          v[j] = __hip_atomic_load(row + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine &= e < 0 || unsigned(v[j] >> 32) == tag;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+        ok = false;
+        break;
+      }
+    } while (!__all(mine));
+  }
+  if (!ok && lane_id() == 0) store_agent(err, 1u);
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) {
+    const int e = L.expert(rp, j);
+    lg[j] = e >= 0 ? __uint_as_float(unsigned(v[j])) + (bias ? bias[e] : 0.0f) : kNegInfF;
+  }
+  return ok;
 }
 
 // sum of the 4 waves' partial row sums; thread r < R gets row r
@@ -283,7 +335,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   __shared__ int sids[kRouteGemvMaxT * 16];
   __shared__ float sw[kRouteGemvMaxT * 16];
   __shared__ unsigned s_next;
-  __shared__ int s_ok, s_last;
+  __shared__ int s_ok, s_last, s_rok;
   const DecodeParams& d = p.d;
   const Ctr c{p.ctr};
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
@@ -293,11 +345,14 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   const unsigned total = unsigned(b3 + n[3]);
   const int q = blockIdx.x % kQ;
   // per-workgroup state (uniform across the workgroup)
-  bool have_r = false, have_topk = false, have_dn_deps = false, poisoned = false;
+  bool have_topk = false, have_dn_deps = false, poisoned = false;
   int pend_f = 0, pend_n = 0;  // finished items of phase pend_f not yet counted
-  auto phase_of = [&](int i) { return i < b2 ? 1 : (i < b3 ? 2 : 3); };
+  auto phase_of = [&](int i) { return i < b2 ? 0 : (i < b3 ? 1 : 2); };
+  const unsigned epoch = __hip_atomic_load(c.epoch(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned tag = epoch % 0xffffffffu + 1u;  // never 0: a zero-filled word is never ready
   for (int i = tid; i < T * H / 8; i += 256)
     reinterpret_cast<u32x4*>(sx)[i] = reinterpret_cast<const u32x4*>(d.x)[i];
+  if (tid == 0) s_rok = 1;
   __syncthreads();
 
   // R: workgroup e < E computes router row e before it joins the queues (the
@@ -305,8 +360,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   // routed item waits for, starts at once)
   if (int(blockIdx.x) < E) {
     if (tid == 0) s_next = q + kQ * atomic_inc(c.head(q));
-    router_row(d.x, T, d.wr, d.rp, blockIdx.x, d.logits, part, true, sx);
-    count_items(c, 0, q, 1, 0, E);
+    router_row(d.x, T, d.wr, d.rp, blockIdx.x, nullptr, part, false, sx, c.tagged(), tag);
   } else if (tid == 0) {
     s_next = q + kQ * atomic_inc(c.head(q));
   }
@@ -323,17 +377,15 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
       gate_up_lds<WF, kSUR, kUC>(sx + size_t(t) * H / 2, H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is);
     } else {
       if (!have_topk) {  // every workgroup routes all T tokens itself (wave t: token t)
-        if (!have_r) {
-          poisoned |= !wait_flag(c, 0, &s_ok);
-          have_r = true;
-        }
         if (wave < T) {
           const TopkLayout L(d.rp, lane);
           float lg[kMpl];
-          topk_load(d.rp, L, d.logits + size_t(wave) * E, d.bias, lg);
+          if (!load_tagged_logits(d.rp, L, c.tagged() + size_t(wave) * E, d.bias, tag, lg, c.error()) && lane == 0)
+            s_rok = 0;
           topk_select(d.rp, L, lg, sids + wave * K, sw + wave * K);
         }
         __syncthreads();
+        poisoned |= s_rok == 0;
         have_topk = true;
       }
       if (it < b3) {  // RG: 8 routed intermediate columns of one (token, slot)
@@ -386,8 +438,8 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
             dn_load_w<WF>(st[j], s[j], n0);
           }
           if (!have_dn_deps) {
-            if (Is) poisoned |= !wait_flag(c, 1, &s_ok);
-            poisoned |= !wait_flag(c, 2, &s_ok);
+            if (Is) poisoned |= !wait_flag(c, 0, &s_ok);
+            poisoned |= !wait_flag(c, 1, &s_ok);
             have_dn_deps = true;
           }
 #pragma unroll
@@ -409,7 +461,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
       }
     }
     const int f = phase_of(it);
-    if (f == 1 || f == 2) {
+    if (f < 2) {
       pend_f = f;
       ++pend_n;
     }
@@ -418,11 +470,12 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
     item = s_next;
     __syncthreads();  // s_next is rewritten only after every thread has read it
     if (pend_n && (item >= total || phase_of(int(item)) != pend_f)) {  // end of a run: count it
-      count_items(c, pend_f, q, pend_n, pend_f == 1 ? b1 : b2, pend_f == 1 ? b2 : b3);
+      count_items(c, pend_f, q, pend_n, pend_f == 0 ? b1 : b2, pend_f == 0 ? b2 : b3);
       pend_n = 0;
     }
   }
-  // exit count; the last workgroup out resets the counter block
+  // exit count; the last workgroup out resets the counters and advances the
+  // epoch (the next launch on this workspace starts after this one ends)
   if (tid == 0) {
     const int G = int(gridDim.x), s = blockIdx.x % kQ;
     const unsigned cnt = unsigned(G / kQ + (s < G % kQ));
@@ -431,8 +484,10 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
     s_last = last;
   }
   __syncthreads();
-  if (s_last)
+  if (s_last) {
     for (int l = 1 + tid; l < kCtrLines; l += 256) store_agent(c.base + l * kLine, 0u);
+    if (tid == 0) store_agent(c.epoch(), epoch + 1u);
+  }
 }
 
 template <int WF>

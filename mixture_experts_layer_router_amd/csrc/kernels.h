@@ -182,7 +182,8 @@ hipError_t launch_decode_stage2(const DecodeParams& p, hipStream_t s);
 // shared experts, in one persistent launch (decode.hip): router, top-k, shared
 // and routed gate/up, down + combine, ordered by work queues and completion
 // counters in `ctr` (kFusedCtrBytes, zero before the first launch; every
-// launch leaves it zero again, except the sticky error word).  d.xs must be
+// launch leaves its queues and counters zero again; the sticky error word,
+// the epoch word and the tagged router logits are kept).  d.xs must be
 // d.x (bf16); d.swfmt must equal wfmt; d.ysh is unused.
 struct FusedDecodeParams {
   DecodeParams d;
@@ -194,6 +195,8 @@ struct FusedDecodeParams {
 };
 constexpr int kFusedCtrBytes = 32768;
 constexpr int kFusedErrorWord = 0;  // ctr[0] != 0: a bounded wait gave up (never expected)
+constexpr int kFusedEpochWord = 1;  // ctr[1]: launches so far (wraps), never reset
+constexpr int kFusedTagOff = 24576;  // bytes: tagged router logits, 64-bit [T][E]
 constexpr int kFusedXLdsMax = 65536;  // bytes of x (T * H bf16) the launch stages in LDS
 hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s);
 

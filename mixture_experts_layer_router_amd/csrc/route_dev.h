@@ -121,10 +121,12 @@ MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[
 // in wave order.  coherent: agent-scope atomic stores of the logits (read by
 // another workgroup in the same launch).
 // xl: when not null, x as bf16 pairs in LDS (token t's row at xl + t * H / 2),
-// read there instead of from x.
+// read there instead of from x.  tagged: when not null, the logits go there
+// instead, as 64-bit words (tag << 32 | float bits) stored with agent-scope
+// atomic stores, so a reader can tell this launch's value from an old one.
 MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* __restrict__ wr, const RouteParams& p,
                         int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT], bool coherent = false,
-                        const uint32_t* xl = nullptr) {
+                        const uint32_t* xl = nullptr, uint64_t* tagged = nullptr, unsigned tag = 0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint16_t* row = wr + size_t(e) * p.H;
   float acc[kRouteGemvMaxT] = {};
@@ -186,7 +188,10 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
   __syncthreads();
   if (tid < T) {
     const float v = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
-    if (coherent)
+    if (tagged)
+      __hip_atomic_store(tagged + tid * p.E + e, (uint64_t(tag) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else if (coherent)
       __hip_atomic_store(logits + tid * p.E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
       logits[tid * p.E + e] = v;

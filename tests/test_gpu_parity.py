@@ -315,14 +315,17 @@ def test_forward_zero_tokens_is_noop():
 
 
 def _queue_words(layer):
-    return layer.ws[:32768].view(torch.int32).cpu().numpy()
+    """Error word, epoch word and counter lines of the single-launch path (the
+    tagged router logits follow them in the first 32 KiB)."""
+    return layer.ws[:24576].view(torch.int32).cpu().numpy()
 
 
 def test_single_launch_queue_across_calls():
     """The single-launch small-T path over many calls on one workspace, with
     T changing between 1 and 4 and two layers interleaved on one stream:
     every output matches the oracle and the queue state is zero after each
-    call (no bounded wait gave up, every counter reset)."""
+    call (no bounded wait gave up, every counter reset) but for the epoch
+    word, which each call advances by one."""
     layers = []
     for name in ("dsv2_like_4tok", "bf16_1tok"):
         cfg = SMALL[name].derive(tokens=4)
@@ -338,7 +341,10 @@ def test_single_launch_queue_across_calls():
             assert np.array_equal(ids.cpu().numpy(), r.ids[:T])
             assert np.max(np.abs(w.cpu().numpy() - r.w[:T]) / r.w[:T]) <= WTOL
             assert rel_err(oracle.bf16_to_f64(out), r.out[:T]) <= TOL
-            assert not _queue_words(layer).any()
+            q = _queue_words(layer)
+            assert q[0] == 0 and q[1] == it + 1
+            q[1] = 0
+            assert not q.any()
 
 
 def test_forward_reuses_workspace_across_sizes():
