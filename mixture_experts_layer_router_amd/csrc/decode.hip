@@ -235,36 +235,42 @@ MOE_DEV void dn_math(const DnStage<WF>& st, const DownSrc& s, float (&acc)[kDR])
   }
 }
 
+// a global-memory pointer the caller knows to be the same in every lane, in
+// scalar registers; typed as global so that loads through it are global
+// loads (a generic pointer would make them flat loads, which also count in
+// the LDS counter, so every wait for an LDS read of x would wait for them)
+#define MOE_GLOBAL __attribute__((address_space(1)))
+MOE_DEV const MOE_GLOBAL uint8_t* uni(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v)));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v >> 32)));
+  return reinterpret_cast<const MOE_GLOBAL uint8_t*>((hi << 32) | lo);
+}
+
+
 // h[i0 .. i0+NR) = SiLU(x.Wg^T) * (x.Wu^T) for the token whose bf16 x row sits
 // in LDS as packed pairs (xl).  NC weight chunks of each of the 2 NR rows are
 // loaded together (at H = 5120 and NC = 5, a wave's whole item in one round
 // trip); x comes from LDS, so the registers hold only weights and scales.  h
 // is stored with agent-scope atomic stores (read by other workgroups inside
-// the launch once the phase is published).
-// a pointer the caller knows to be the same in every lane, in scalar registers
-MOE_DEV const uint8_t* uni(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v)));
-  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v >> 32)));
-  return reinterpret_cast<const uint8_t*>((hi << 32) | lo);
-}
-
-template <int WF, int NR, int NC>
+// the launch once the phase is published).  pre() runs once every load has
+// been consumed and before the store.
+template <int WF, int NR, int NC, class Pre>
 MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u, const void* gs, const void* us,
-                         int i0, float* hrow) {
+                         int i0, float* hrow, Pre pre) {
   constexpr int CW = Fmt<WF>::CW, EPL = Fmt<WF>::EPL, ES = Fmt<WF>::ES;
   constexpr int NS = WF == W_MXFP8 ? NR : 1;  // scales per chunk (FP8_B128: the rows share a 128-row block)
   const int lane = lane_id();
   // row bases are uniform (scalar registers); each lane adds a 32-bit offset
-  const uint8_t* gb[NR];
-  const uint8_t* ub[NR];
+  const MOE_GLOBAL uint8_t* gb[NR];
+  const MOE_GLOBAL uint8_t* ub[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     gb[r] = uni(static_cast<const uint8_t*>(g) + size_t(i0 + r) * H * ES);
     ub[r] = uni(static_cast<const uint8_t*>(u) + size_t(i0 + r) * H * ES);
   }
-  const uint8_t* gsb = nullptr;
-  const uint8_t* usb = nullptr;
+  const MOE_GLOBAL uint8_t* gsb = nullptr;
+  const MOE_GLOBAL uint8_t* usb = nullptr;
   if (WF == W_FP8_B128) {  // the 128-row block's scale row
     gsb = uni(static_cast<const uint8_t*>(gs) + size_t(i0 >> 7) * (H >> 7) * 4);
     usb = uni(static_cast<const uint8_t*>(us) + size_t(i0 >> 7) * (H >> 7) * 4);
@@ -280,12 +286,12 @@ MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u
       const uint32_t k = uint32_t(min(k0 + c * CW + kl, H - EPL));
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        wg[c][r] = *reinterpret_cast<const u32x4*>(gb[r] + k * ES);
-        wu[c][r] = *reinterpret_cast<const u32x4*>(ub[r] + k * ES);
+        wg[c][r] = *reinterpret_cast<const MOE_GLOBAL u32x4*>(gb[r] + k * ES);
+        wu[c][r] = *reinterpret_cast<const MOE_GLOBAL u32x4*>(ub[r] + k * ES);
       }
       if (WF == W_FP8_B128) {
-        sg[c][0] = *reinterpret_cast<const float*>(gsb + (k >> 7) * 4);
-        su[c][0] = *reinterpret_cast<const float*>(usb + (k >> 7) * 4);
+        sg[c][0] = *reinterpret_cast<const MOE_GLOBAL float*>(gsb + (k >> 7) * 4);
+        su[c][0] = *reinterpret_cast<const MOE_GLOBAL float*>(usb + (k >> 7) * 4);
       } else {
 #pragma unroll
         for (int r = 0; r < NS; ++r) {
@@ -323,6 +329,7 @@ MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u
     const float uv = wave_sum(au[r]);
     if (lane == r) mine = silu(gv) * uv;
   }
+  pre();
   if (lane < NR) __hip_atomic_store(hrow + i0 + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -366,15 +373,22 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   }
   __syncthreads();
   unsigned item = s_next, next = 0;
+  __syncthreads();  // thread 0 writes s_next again (first item) only after every thread has read it
   while (item < total) {
-    // claim the next item now; its value is only needed (and waited for) when
-    // it is handed to the workgroup at the end of this one
+    // claim the next item now; thread 0 hands it to the workgroup (s_next)
+    // once this item's loads are consumed and before its stores are issued:
+    // stores share the counter that the wait for the claim's value uses, so
+    // a later hand-over would also wait for the stores to complete
     if (tid == 0) next = atomic_inc(c.head(q));
+    auto hand_over = [&] {
+      if (tid == 0) s_next = q + kQ * next;
+    };
     const int it = int(item);
     if (it < b2) {  // SU: 8 shared intermediate columns of one token
       const int i = it - b1, per = Is / kSUpCols;
       const int t = i / per, c0 = (i % per) * kSUpCols + wave * kSUR;
-      gate_up_lds<WF, kSUR, kUC>(sx + size_t(t) * H / 2, H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is);
+      gate_up_lds<WF, kSUR, kUC>(sx + size_t(t) * H / 2, H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is,
+                                 hand_over);
     } else {
       if (!have_topk) {  // every workgroup routes all T tokens itself (wave t: token t)
         if (wave < T) {
@@ -402,7 +416,8 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
         const uint8_t* ue = static_cast<const uint8_t*>(p.u) + e * ws;
         const uint8_t* gse = p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr;
         const uint8_t* use = p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr;
-        gate_up_lds<WF, kUR, kUC>(sx + size_t(slot / K) * H / 2, H, ge, ue, gse, use, c0, p.h + size_t(slot) * I);
+        gate_up_lds<WF, kUR, kUC>(sx + size_t(slot / K) * H / 2, H, ge, ue, gse, use, c0, p.h + size_t(slot) * I,
+                                  hand_over);
       } else {  // DN: kDR output rows of one token over [shared Is | routed K*I]
         const int i = it - b3, nb = H / kDR;
         const int t = i / nb, n0 = (i % nb) * kDR;
@@ -457,6 +472,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
           for (int j = 0; j < kDJ; ++j) dn_math<WF>(st[j], s[j], acc);
         }
         const float v = rows_reduce<kDR>(acc, dpart, wave, lane);
+        hand_over();
         if (tid < kDR) p.out[size_t(t) * H + n0 + tid] = poisoned ? uint16_t(0x7fc0) : f32_to_bf16(v);
       }
     }
@@ -465,7 +481,6 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
       pend_f = f;
       ++pend_n;
     }
-    if (tid == 0) s_next = q + kQ * next;
     __syncthreads();
     item = s_next;
     __syncthreads();  // s_next is rewritten only after every thread has read it
