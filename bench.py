@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--secondary-only", action="store_true",
                     help="only run the 2048-token workload (for profiling its kernels)")
+    ap.add_argument("--batched-only", metavar="NAME", choices=("dsv2_256tok", "dsv2_4096tok_zipf"),
+                    help="only run one batched workload (for profiling its kernels)")
     ap.add_argument("--sources-hash", metavar="KERNEL", help="print the sources hash recorded with KERNEL's counters")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (a known-size reference for HBM counters)")
@@ -132,6 +134,9 @@ def main():
         return
     if args.secondary_only:
         print(json.dumps({"secondary": secondary(args, moe, synth, torch)}), flush=True)
+        return
+    if args.batched_only:
+        print(json.dumps({"batched": batched(moe, synth, torch, names=(args.batched_only,))}), flush=True)
         return
     cfg = synth.get_config("dsv2_b1")
     reps = [synth.make_inputs(cfg, dev, replica=r) for r in range(args.replicas)]
@@ -252,14 +257,14 @@ def measured_traffic(kernel):
     return int(fields["traffic_bytes"])
 
 
-def batched(moe, synth, torch, steps=20):
+def batched(moe, synth, torch, steps=20, names=("dsv2_256tok", "dsv2_4096tok_zipf")):
     """The DeepSeek-V2 FP8 layer at 256 tokens (near-uniform routing) and at
     4,096 tokens (Zipf-skewed routing): us/layer, the HBM rate of the bytes
     the routing touches (weights of the touched experts, shared expert,
     router, x and out) and the matrix rate of the flops over real rows.
     Both working sets exceed the 256 MB memory-side cache."""
     res = []
-    for name in ("dsv2_256tok", "dsv2_4096tok_zipf"):
+    for name in names:
         cfg = synth.get_config(name)
         inp = synth.make_inputs(cfg, "cuda:0")
         lay = moe.Layer(cfg, inp)
