@@ -37,14 +37,16 @@
 // brings the counter to the phase's item count raises the phase's ready flag.
 // Waiters poll only the flag (a line no atomic touches).  A workgroup never
 // waits while it holds uncounted items, so nothing waits on itself.
-// Cross-workgroup data (logits, ids / weights, h) is written with
-// device-scope atomic stores; a producer waits for its stores (vmcnt(0))
-// before its increment.  A consumer reads the data with plain loads after
-// seeing the flag: its XCD's L2 cannot hold those lines yet, since nothing
-// reads them before the flag rises and every launch starts with clean L2s.
-// No L2 writeback or invalidate is needed.  Waits are bounded (about 0.2 s):
-// a wait that gives up sets the error word and the workgroup writes NaN for
-// its outputs.  The last workgroup to exit resets every counter and flag.
+// Cross-workgroup data (ids / weights, h) is written with device-scope
+// atomic stores; a producer waits for its stores (vmcnt(0)) before its
+// increment.  A consumer reads the data with plain loads after seeing the
+// flag: its XCD's L2 cannot hold those lines yet, since nothing reads them
+// before the flag rises and every launch starts with clean L2s.  No L2
+// writeback or invalidate is needed.  The tagged logits, which are polled
+// before they are ready, are read with device-scope loads instead.  Waits
+// are bounded (about 0.2 s): a wait that gives up sets the error word and the
+// workgroup writes NaN for its outputs.  The last workgroup to exit resets
+// every counter and flag and advances the epoch.
 #include <algorithm>
 
 #include "gemv_dev.h"
