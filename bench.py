@@ -82,6 +82,8 @@ class HostExperts:
 
 
 def time_layers(layers, xs, steps, warmup, torch):
+    """Mean ms per step over `steps` back-to-back steps (events on the launch
+    stream around the loop), and the wall-clock ms per step."""
     n = len(layers)
     for i in range(warmup):
         layers[i % n].forward(xs[i % n])
@@ -95,6 +97,33 @@ def time_layers(layers, xs, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(stop) / steps, wall / steps * 1e3
+
+
+def block_stats(layers, xs, blocks, per_block, torch):
+    """Median, p10 and p90 (us per step) over `blocks` runs of `per_block`
+    back-to-back steps, each run between its own two events (the median over
+    runs of "Benchmarking Honestly"; runs of several steps keep the events'
+    own gaps out of the per-step figure)."""
+    n = len(layers)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * blocks)]
+    i = 0
+    for b in range(blocks):
+        ev[2 * b].record()
+        for _ in range(per_block):
+            layers[i % n].forward(xs[i % n])
+            i += 1
+        ev[2 * b + 1].record()
+    torch.cuda.synchronize()
+    us = sorted(ev[2 * b].elapsed_time(ev[2 * b + 1]) * 1e3 / per_block for b in range(blocks))
+    q = lambda f: us[min(len(us) - 1, int(round(f * (len(us) - 1))))]
+    return {"median": round(statistics.median(us), 3), "p10": round(q(0.1), 3), "p90": round(q(0.9), 3),
+            "runs": blocks, "steps_per_run": per_block}
+
+
+def check_workspaces(layers, moe):
+    """Every single-launch call's bounded waits completed (raises otherwise)."""
+    for lay in layers:
+        moe.workspace_check(lay.ws)
 
 
 def trace_kernels(layers, xs, steps, moe, torch):
@@ -120,6 +149,7 @@ def main():
     import numpy as np
     import torch
 
+    import numpy as np
     import mixture_experts_layer_router_amd as moe
     import synth
 
@@ -146,6 +176,8 @@ def main():
 
     ms_step, wall_ms = time_layers(layers, xs, args.steps, args.warmup, torch)
     us = ms_step * 1e3
+    stats = block_stats(layers, xs, 20, 10, torch)
+    check_workspaces(layers, moe)
 
     # algorithmic bytes per step, from each replica's actual routing
     step_bytes, gu_bytes = [], []
@@ -196,6 +228,7 @@ def main():
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": int(bytes_step),
         "wall_ms_per_step": round(wall_ms, 6),
+        "step_us_stats": stats,
         "kernels_us": {k: round(v[0] * 1e3, 3) for k, v in kern.items()},
         "roofline": {
             "kernel": dom,
@@ -210,6 +243,7 @@ def main():
         },
     }
 
+    out["tiny"] = tiny(moe, synth, torch)
     if not args.no_secondary:
         out["secondary"] = secondary(args, moe, synth, torch)
     if not args.no_small_m:
@@ -227,6 +261,8 @@ def main():
 # while these files are unchanged
 KERNEL_SOURCES = {
     "decode_fused": ("decode.hip", "gemv_dev.h", "route_dev.h", "common.h", "kernels.h"),
+    "gemm_gate_up_routed": ("gemm.hip", "gemm2.hip", "gemm_dev.h", "common.h", "kernels.h"),
+    "gemm_down_routed": ("gemm.hip", "gemm2.hip", "gemm_dev.h", "common.h", "kernels.h"),
 }
 
 
@@ -241,10 +277,11 @@ def csrc_hash(kernel):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary of `kernel`, or
-    None when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_dsv2_b1_hbm_counters.txt")
+def measured_traffic(kernel, workload="dsv2_b1"):
+    """HBM bytes per launch from the committed counter summary of `kernel` on
+    `workload`, or None when the kernel sources changed since the counters
+    were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -257,12 +294,26 @@ def measured_traffic(kernel):
     return int(fields["traffic_bytes"])
 
 
+def gemm_roofline(workload, kern, rows, H, I, kernel):
+    """Roofline of a grouped FFN GEMM launch: flops over the real rows
+    (gate/up: 2 * rows * 2I * H; down: 2 * rows * H * I) over the launch's
+    average duration (events on the launch stream), against the dense FP8
+    matrix peak; traffic from the committed counter summary, if current."""
+    flops = 2.0 * rows * (2 * I if "gate_up" in kernel else I) * H
+    us = kern[kernel][0] * 1e3
+    achieved = flops / (us * 1e-6) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(kernel, workload), "flops_per_launch": flops, "launch_us": round(us, 2)}
+
+
 def batched(moe, synth, torch, steps=20, names=("dsv2_256tok", "dsv2_4096tok_zipf")):
     """The DeepSeek-V2 FP8 layer at 256 tokens (near-uniform routing) and at
     4,096 tokens (Zipf-skewed routing): us/layer, the HBM rate of the bytes
     the routing touches (weights of the touched experts, shared expert,
     router, x and out) and the matrix rate of the flops over real rows.
     Both working sets exceed the 256 MB memory-side cache."""
+    import numpy as np
     res = []
     for name in names:
         cfg = synth.get_config(name)
@@ -277,7 +328,10 @@ def batched(moe, synth, torch, steps=20, names=("dsv2_256tok", "dsv2_4096tok_zip
                   inp.x.numel() * 2 * 2)
         flops = 2.0 * T * K * 3 * H * I + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
         kern = trace_kernels([lay], [inp.x], 3, moe, torch)
+        cnt = np.bincount(ids.flatten().cpu().numpy(), minlength=E)
         res.append({"workload": name, "tokens": T, "us_per_layer": round(ms * 1e3, 2),
+                    "max_mean_load": round(float(cnt.max() / cnt.mean()), 2), "empty_experts": int((cnt == 0).sum()),
+                    "roofline": gemm_roofline(name, kern, T * K, H, I, "gemm_gate_up_routed"),
                     "touched_experts": len(touched), "algorithmic_bytes": int(nbytes),
                     "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -299,6 +353,7 @@ def small_m(moe, synth, torch, tokens=(2, 4, 8), replicas=8):
         reps = [synth.make_inputs(cfg, "cuda:0", replica=r) for r in range(replicas)]
         layers = [moe.Layer(cfg, inp) for inp in reps]
         ms, _ = time_layers(layers, [inp.x for inp in reps], 100, 10, torch)
+        check_workspaces(layers, moe)
         nbytes = []
         for lay, inp in zip(layers, reps):
             _, ids, _ = lay.forward()
@@ -315,6 +370,20 @@ def small_m(moe, synth, torch, tokens=(2, 4, 8), replicas=8):
     return res
 
 
+def tiny(moe, synth, torch, replicas=8):
+    """The tiny 8-token bf16 layer (hidden 256, 16 experts): launch-latency
+    bound; us per layer over 8 replicas cycled."""
+    cfg = synth.get_config("tiny_8tok")
+    reps = [synth.make_inputs(cfg, "cuda:0", replica=r) for r in range(replicas)]
+    layers = [moe.Layer(cfg, inp) for inp in reps]
+    ms, _ = time_layers(layers, [inp.x for inp in reps], 200, 20, torch)
+    return {"workload": "tiny_8tok: 8 tokens, H=256, 16 experts (4 groups, top-2 groups, top-4), I=128, bf16",
+            "us_per_layer": round(ms * 1e3, 2), "step_us_stats": block_stats(layers, [inp.x for inp in reps], 20, 10,
+                                                                              torch),
+            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in trace_kernels(layers, [i.x for i in reps], 8, moe,
+                                                                               torch).items()}}
+
+
 def secondary(args, moe, synth, torch):
     cfg = synth.get_config("h7168_2048tok_mx")
     inp = synth.make_inputs(cfg, "cuda:0")
@@ -324,11 +393,14 @@ def secondary(args, moe, synth, torch):
     flops = 2.0 * T * K * 3 * H * I + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
     tflops = flops / (ms * 1e-3) / 1e12
     kern = trace_kernels([lay], [inp.x], 5, moe, torch)
+    stats = block_stats([lay], [inp.x], 10, 5, torch)
     del lay, inp
     torch.cuda.empty_cache()
     return {
         "workload": "2,048 tokens, H=7168, 32 experts flat top-4, I=2048, MXFP8 routed (e8m0 1x32) + bf16 shared 2048",
         "us_per_layer": round(ms * 1e3, 2),
+        "step_us_stats": stats,
+        "roofline": gemm_roofline("h7168_2048tok_mx", kern, T * K, H, I, "gemm_gate_up_routed"),
         "tflops": round(tflops, 1),
         "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
         "flops_per_layer": flops,

@@ -46,6 +46,9 @@
  *                       activation format pair that no kernel implements
  *     MOE_EWORKSPACE    ws_bytes below moe_workspace_size()
  *     MOE_EHIP          a HIP launch failed
+ *     MOE_EWAIT         (moe_workspace_check only) a bounded wait inside a
+ *                       single-launch moe_forward gave up; that call's
+ *                       output holds NaN rows
  *   T = 0 is a no-op returning MOE_OK.
  */
 #ifndef MOE_MI355X_H
@@ -65,7 +68,8 @@ typedef enum {
   MOE_EUNSUPPORTED = 2,
   MOE_EALIGN = 3,
   MOE_EWORKSPACE = 4,
-  MOE_EHIP = 5
+  MOE_EHIP = 5,
+  MOE_EWAIT = 6
 } moe_status;
 
 /* Weight formats (DSV2-236B-MegaKernel README, "Results": per-128
@@ -136,7 +140,11 @@ moe_status moe_workspace_size(const moe_config* cfg /*host*/, int32_t max_tokens
  * x bf16 [T][H]; w_router bf16 [E][H]; bias fp32 [E] or NULL (added to the
  * logits before the softmax).  Outputs topk_ids int32 [T][K] in descending
  * score order (ties to the lower id) and topk_w fp32 [T][K] =
- * route_scale * score (no renormalisation over the selected experts). */
+ * route_scale * score (no renormalisation over the selected experts).
+ * Every id is in [0, E), whatever the logits: -inf logits (a masking bias)
+ * tie below every finite logit, lowest id first, with weight 0; a token with
+ * a NaN or +inf logit has no defined softmax, takes the lowest ids of the
+ * lowest groups and gets NaN weights. */
 moe_status moe_route(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
                      const uint16_t* w_router, const float* bias, int32_t* topk_ids,
                      float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -191,12 +199,16 @@ moe_status moe_combine(const moe_config* cfg /*host*/, const float* y_perm, cons
  * shared gate/up, routed gate/up and down+combine items in that order from
  * queues in the workspace, and wait (bounded) only for earlier items.
  * Waits give up after about 0.2 s: int32 word 0 of the workspace then
- * becomes nonzero (sticky) and the rows of `out` written by the workgroup
- * that gave up are NaN.  With the device to itself a wait lasts microseconds;
- * the queue order keeps the launch free of deadlock whatever number of its
- * workgroups are resident (at least 32).  Other T <= 4 cases run
- * in four to six launches, T <= 4 never needs more; larger T runs the
- * dispatch + grouped-GEMM path (or the GEMV path for formats it lacks). */
+ * becomes nonzero (sticky; moe_workspace_check reports and clears it) and
+ * the rows of `out` written by the workgroup that gave up are NaN.  With the
+ * device to itself a wait lasts microseconds.  Progress needs at least
+ * max(E, 32) of the launch's workgroups resident at once (the first E take
+ * the router rows, and each of 32 queues needs a resident server); the
+ * launch asks for the device's full resident capacity, so only a kernel on
+ * another stream that holds most of the CUs for longer than the wait bound
+ * can make a wait give up.  Other T <= 4 cases run in four to six launches;
+ * larger T runs the dispatch + grouped-GEMM path (or the GEMV path for
+ * formats it lacks). */
 moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
                        const uint16_t* w_router, const float* bias,
                        const moe_ffn_weights* routed /*host struct*/,
@@ -204,11 +216,31 @@ moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_
                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Reports the sticky error word of a workspace used by moe_forward's
+ * single-launch path: MOE_EWAIT if a bounded wait of an earlier call gave up
+ * (its output rows are NaN), else MOE_OK.  clear != 0 resets the word.
+ * Host-synchronising: it copies the word to the host after the work queued on
+ * `stream` so far and waits for that copy, so it is not for use under graph
+ * capture.  MOE_EINVAL for a null ws or ws_bytes below 4. */
+moe_status moe_workspace_check(void* ws, size_t ws_bytes, int32_t clear, hipStream_t stream);
+
 /* Diagnostics of the device FP8 codec (the conversions every kernel uses):
  * decode n e4m3 codes to fp32, and encode n fp32 values with the library's
  * round-to-nearest-even saturating rule.  For tests of the codec itself. */
 moe_status moe_debug_e4m3_decode(const uint8_t* codes, float* out, int32_t n, hipStream_t stream);
 moe_status moe_debug_e4m3_encode(const float* in, uint8_t* codes, int32_t n, hipStream_t stream);
+
+/* Test hooks.  moe_debug_ws_offset: byte offset, inside a workspace planned
+ * for max_tokens tokens, of a region that moe_forward's batched path fills:
+ * region 0 expert_offsets int32 [E+1], 1 perm_src int32 [T*K], 2 inv_pos
+ * int32 [T*K], 3 the grouped-GEMM tile list int32 [2 * n_tiles] (expert,
+ * first row of the tile within the expert's segment), 4 n_tiles int32.
+ * moe_debug_ffn_tile_rows: rows per tile of the grouped GEMMs that the
+ * routed (which = 0) or shared (1) FFN runs on at batched sizes (256: the
+ * large-tile kernel, 128: the other), or -1 for an invalid config. */
+moe_status moe_debug_ws_offset(const moe_config* cfg /*host*/, int32_t max_tokens, int32_t region,
+                               size_t* offset /*host*/);
+int32_t moe_debug_ffn_tile_rows(const moe_config* cfg /*host*/, int32_t which);
 
 /* Measurement hook: arm (events != NULL, n_events >= 2) or disarm (NULL) a
  * launch trace.  While armed, each kernel launch of the entry points records

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libmoe.so")
 WFMT = {"bf16": 0, "fp8_b128": 1, "mxfp8": 2}
 AFMT = {"none": 0, "fp8_1x128": 1, "mxfp8_1x32": 2}
 
-STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EALIGN", 4: "MOE_EWORKSPACE", 5: "MOE_EHIP"}
+STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EALIGN", 4: "MOE_EWORKSPACE", 5: "MOE_EHIP",
+          6: "MOE_EWAIT"}
 
 
 class MoEError(RuntimeError):
@@ -61,6 +62,9 @@ def _lib():
             "moe_combine": (_i32, [P(Config), _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
             "moe_forward": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
+            "moe_workspace_check": (_i32, [_vp, _sz, _i32, _vp]),
+            "moe_debug_ws_offset": (_i32, [P(Config), _i32, _i32, P(_sz)]),
+            "moe_debug_ffn_tile_rows": (_i32, [P(Config), _i32]),
             "moe_debug_e4m3_decode": (_i32, [_vp, _vp, _i32, _vp]),
             "moe_debug_e4m3_encode": (_i32, [_vp, _vp, _i32, _vp]),
             "moe_debug_trace": (_i32, [_vp, _i32]),
@@ -75,7 +79,8 @@ def _lib():
 
 
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
+           "moe_combine", "moe_forward", "moe_workspace_check", "moe_debug_ws_offset",
+           "moe_debug_ffn_tile_rows", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
            "moe_debug_trace_count", "moe_debug_trace_name")
 
 
@@ -153,6 +158,27 @@ def forward(cfg, x, w_router, bias, routed, shared, out, ids, w, ws, stream=None
     _check(_lib().moe_forward(ctypes.byref(cfg), _ptr(x), x.shape[0], _ptr(w_router), _ptr(bias),
                               ctypes.byref(routed), None if shared is None else ctypes.byref(shared), _ptr(out),
                               _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)), "moe_forward")
+
+
+def workspace_check(ws, clear=True, stream=None):
+    """Raise MoEError(MOE_EWAIT) if a bounded wait of the single-launch path
+    gave up in an earlier call on this workspace (synchronises the stream)."""
+    _check(_lib().moe_workspace_check(_ptr(ws), ws.numel(), int(bool(clear)), _stream(stream)), "moe_workspace_check")
+
+
+WS_REGIONS = {"offsets": 0, "perm_src": 1, "inv_pos": 2, "tiles": 3, "ntiles": 4}
+
+
+def ws_region(cfg, max_tokens, ws, name, count):
+    """int32 view of `count` entries of a dispatch region of a workspace (test hook)."""
+    off = ctypes.c_size_t(0)
+    _check(_lib().moe_debug_ws_offset(ctypes.byref(cfg), int(max_tokens), WS_REGIONS[name], ctypes.byref(off)),
+           "moe_debug_ws_offset")
+    return ws[off.value:off.value + 4 * count].view(torch.int32)
+
+
+def ffn_tile_rows(cfg, which):
+    return _lib().moe_debug_ffn_tile_rows(ctypes.byref(cfg), int(which))
 
 
 def e4m3_decode(codes, out, stream=None):

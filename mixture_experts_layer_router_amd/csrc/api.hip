@@ -202,6 +202,24 @@ SideStream* side_stream(hipStream_t caller) {
   return &ss;
 }
 
+// Joins the side stream back into the caller's stream when it goes out of
+// scope, so a call that returns early after the fork (a failed launch) still
+// leaves the caller's stream ordered after the side stream's work on x and
+// the workspace.  join() does it early, before the combine.
+struct SideJoin {
+  SideStream* side = nullptr;
+  hipStream_t caller = nullptr;
+  hipError_t join() {
+    if (!side) return hipSuccess;
+    SideStream* s = side;
+    side = nullptr;
+    const hipError_t e = hipEventRecord(s->join, s->s);
+    const hipError_t f = hipStreamWaitEvent(caller, s->join, 0);
+    return e != hipSuccess ? e : f;
+  }
+  ~SideJoin() { (void)join(); }
+};
+
 template <class F>
 hipError_t traced(const char* name, hipStream_t s, F&& f) {
   if (!g_trace.ev || 2 * g_trace.n + 1 >= g_trace.max || g_trace.n >= 128) return f();
@@ -333,6 +351,7 @@ const char* moe_status_string(int32_t st) {
     case MOE_EALIGN: return "MOE_EALIGN: pointer or dimension misaligned";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
     case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+    case MOE_EWAIT: return "MOE_EWAIT: a bounded wait of the single-launch path gave up (NaN output rows)";
     default: return "unknown moe_status";
   }
 }
@@ -644,6 +663,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
   // same CUs).
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
+  SideJoin joiner;  // declared after the lock: it joins before the lock is released
   float* ysh = nullptr;
   if (!gemv && has_shared &&
       long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128) {
@@ -652,8 +672,9 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
     if (side) {
       HIP_TRY(hipEventRecord(side->fork, stream));
       HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
+      joiner.side = side;
+      joiner.caller = stream;
       if ((st = shared_ffn(cfg, x, T, shared, ws, L, &ysh, side->s)) != MOE_OK) return st;
-      HIP_TRY(hipEventRecord(side->join, side->s));
     }
   }
 
@@ -763,9 +784,43 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
                        at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
       return st;
   }
-  if (side) HIP_TRY(hipStreamWaitEvent(stream, side->join, 0));
+  HIP_TRY(joiner.join());
   LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
   return MOE_OK;
+}
+
+moe_status moe_debug_ws_offset(const moe_config* cfg, int32_t max_tokens, int32_t region, size_t* offset) {
+  if (!offset || max_tokens < 0) return MOE_EINVAL;
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const Ws L = plan(cfg, max_tokens);
+  switch (region) {
+    case 0: *offset = L.offsets; return MOE_OK;
+    case 1: *offset = L.perm; return MOE_OK;
+    case 2: *offset = L.inv; return MOE_OK;
+    case 3: *offset = L.tiles; return MOE_OK;
+    case 4: *offset = L.ntiles; return MOE_OK;
+    default: return MOE_EINVAL;
+  }
+}
+
+int32_t moe_debug_ffn_tile_rows(const moe_config* cfg, int32_t which) {
+  if (check_cfg(cfg) != MOE_OK || (which != 0 && which != 1)) return -1;
+  return which == 0 ? ffn_tile_rows(cfg->routed_wfmt, cfg->hidden, cfg->inter)
+                    : ffn_tile_rows(cfg->shared_wfmt, cfg->hidden, cfg->shared_inter);
+}
+
+moe_status moe_workspace_check(void* ws, size_t ws_bytes, int32_t clear, hipStream_t stream) {
+  if (!ws || ws_bytes < 4) return MOE_EINVAL;
+  uint32_t word = 0;
+  HIP_TRY(hipMemcpyAsync(&word, ws, 4, hipMemcpyDeviceToHost, stream));
+  HIP_TRY(hipStreamSynchronize(stream));
+  if (word && clear) {
+    static const uint32_t zero = 0;
+    HIP_TRY(hipMemcpyAsync(ws, &zero, 4, hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+  }
+  return word ? MOE_EWAIT : MOE_OK;
 }
 
 moe_status moe_debug_trace(hipEvent_t* events, int32_t n_events) {

@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   int pend_f = 0, pend_n = 0;  // finished items of phase pend_f not yet counted
   auto phase_of = [&](int i) { return i < b2 ? 0 : (i < b3 ? 1 : 2); };
   const unsigned epoch = __hip_atomic_load(c.epoch(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned tag = epoch % 0xffffffffu + 1u;  // never 0: a zero-filled word is never ready
+  const unsigned tag = epoch % 0xffffffffu + 1u;  // in [1, 0xffffffff]: a zero-filled word is never ready
   for (int i = tid; i < T * H / 8; i += 256)
     reinterpret_cast<u32x4*>(sx)[i] = reinterpret_cast<const u32x4*>(d.x)[i];
   if (tid == 0) s_rok = 1;
@@ -505,7 +505,9 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   __syncthreads();
   if (s_last) {
     for (int l = 1 + tid; l < kCtrLines; l += 256) store_agent(c.base + l * kLine, 0u);
-    if (tid == 0) store_agent(c.epoch(), epoch + 1u);
+    // modulo 0xffffffff: the epoch never reaches 0xffffffff, so consecutive
+    // launches always get different tags (tag = epoch + 1)
+    if (tid == 0) store_agent(c.epoch(), (epoch + 1u) % 0xffffffffu);
   }
 }
 

@@ -195,7 +195,7 @@ struct FusedDecodeParams {
 };
 constexpr int kFusedCtrBytes = 32768;
 constexpr int kFusedErrorWord = 0;  // ctr[0] != 0: a bounded wait gave up (never expected)
-constexpr int kFusedEpochWord = 1;  // ctr[1]: launches so far (wraps), never reset
+constexpr int kFusedEpochWord = 1;  // ctr[1]: launches so far modulo 0xffffffff, never reset
 constexpr int kFusedTagOff = 24576;  // bytes: tagged router logits, 64-bit [T][E]
 constexpr int kFusedXLdsMax = 65536;  // bytes of x (T * H bf16) the launch stages in LDS
 hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s);

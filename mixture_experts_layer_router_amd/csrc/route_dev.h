@@ -55,54 +55,71 @@ struct TopkLayout {
   }
 };
 
-// One wave routes one token.  lg[j]: logit (bias included) of layout slot j,
-// -inf for empty slots.  Writes ids[0..K) and w[0..K) (lane 0).
+// One wave routes one token.  lg[j]: logit (bias included) of layout slot j
+// (empty slots are ignored whatever they hold).  Writes ids[0..K) and w[0..K)
+// (lane 0).
 //   softmax over all experts; group score = max member; top-TG groups by
 //   rank (ties to the lower group); then K rounds of (largest logit among the
 //   kept groups' experts, ties to the lower id).  w = scale * softmax score.
+// Every id written is a member of a kept group, so it lies in [0, E), for any
+// logits: -inf logits are candidates that tie (lowest ids first) below every
+// finite one, and a token whose softmax is undefined (a NaN or +inf logit)
+// has all its candidates tie, so it takes the lowest ids of the lowest
+// groups; its weights are NaN.
 // COH: agent-scope atomic stores of ids / w (read by other workgroups in the same launch).
 template <bool COH = false>
 MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[kMpl], int* ids, float* w) {
   const int lane = lane_id();
+  unsigned live = 0;  // bit j: slot j holds an expert
+  bool bad = false;   // a NaN or +inf logit
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j)
+    if (L.expert(p, j) >= 0) {
+      live |= 1u << j;
+      bad |= !(lg[j] == lg[j]) || lg[j] == INFINITY;
+    } else {
+      lg[j] = kNegInfF;
+    }
   float mx = kNegInfF;
 #pragma unroll
   for (int j = 0; j < kMpl; ++j) mx = fmaxf(mx, lg[j]);
-  const float gmax = lanes_max(mx, L.lpg);  // this lane's group maximum
   const float m = wave_max(mx);
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < kMpl; ++j)
-    if (lg[j] != kNegInfF) se += expf(lg[j] - m);
+    if (lg[j] != kNegInfF) se += expf(lg[j] - m);  // NaN and +inf make s NaN
   const float s = wave_sum(se);
+  // selection keys: the logits, or all equal when the softmax is undefined
+  float key[kMpl];
+  const bool degenerate = __any(bad);
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) key[j] = degenerate ? kNegInfF : lg[j];
+  float kmx = kNegInfF;
+#pragma unroll
+  for (int j = 0; j < kMpl; ++j) kmx = fmaxf(kmx, key[j]);
+  const float gmax = lanes_max(kmx, L.lpg);  // this lane's group maximum
   // rank of this lane's group among the G group maxima
   int grank = 0;
   for (int q = 0; q < p.G; ++q) {
     const float o = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gmax), q * L.lpg));
     grank += (o > gmax) || (o == gmax && q < L.g);
   }
-  const bool kept = L.g < p.G && grank < p.TG;
-#pragma unroll
-  for (int j = 0; j < kMpl; ++j)
-    if (!kept) lg[j] = kNegInfF;
+  if (!(L.g < p.G && grank < p.TG)) live = 0;
   for (int r = 0; r < p.K; ++r) {
     float best = kNegInfF;
-    int bj = 0;
+    int bj = -1;
 #pragma unroll
     for (int j = 0; j < kMpl; ++j)
-      if (lg[j] > best) {  // strict: the lower slot (lower id) wins ties
-        best = lg[j];
+      if (((live >> j) & 1u) && (bj < 0 || key[j] > best)) {  // strict: the lower slot (lower id) wins ties
+        best = key[j];
         bj = j;
       }
     const float v = wave_max(best);
-    const int mine = (best == v && best != kNegInfF) ? L.expert(p, bj) : 0x7fffffff;
-    const int e = wave_min_i(mine);
-    if (mine == e) {
-#pragma unroll
-      for (int j = 0; j < kMpl; ++j)
-        if (j == bj) lg[j] = kNegInfF;
-    }
+    const int mine = (bj >= 0 && best == v) ? L.expert(p, bj) : 0x7fffffff;
+    const int e = wave_min_i(mine);  // a candidate always exists: K <= TG * E / G
+    if (mine == e) live &= ~(1u << bj);
     if (lane == 0) {
-      const float wr = p.scale * (expf(v - m) / s);
+      const float wr = p.scale * (expf(v - m) / s);  // s is NaN for a degenerate token
       if (COH) {
         __hip_atomic_store(ids + r, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(w + r, wr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -31,6 +31,8 @@ Parity status: every function below is pinned by CPU tests (brute-force
 top-k, library argsort/bincount, SwiGLU closed form, dense-masked layer,
 split-vs-fused shared expert, on-grid quantiser identity).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from itertools import combinations
 from typing import Optional
@@ -66,18 +68,51 @@ def dequant_weight(codes, scales, fmt):
     """
     if fmt == "bf16":
         return bf16_to_f64(codes)
-    q = _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
-    N, K = q.shape
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    out = np.empty((N, K))
     if fmt == "fp8_b128":
         s = np.asarray(scales, dtype=np.float32).astype(np.float64)
-        return (q.reshape(N // 128, 128, K // 128, 128) * s[:, None, :, None]).reshape(N, K)
-    if fmt == "mxfp8":
+
+        def rows(a, b):   # 128-row blocks a..b
+            q = _E4M3_TABLE[codes[a * 128:b * 128]]
+            out[a * 128:b * 128] = (q.reshape(b - a, 128, K // 128, 128) * s[a:b, None, :, None]).reshape(-1, K)
+        nblk = N // 128
+    elif fmt == "mxfp8":
         s = e8m0_decode(scales)
-        return (q.reshape(N, K // 32, 32) * s[:, :, None]).reshape(N, K)
-    raise ValueError(fmt)
+
+        def rows(a, b):   # rows a..b
+            q = _E4M3_TABLE[codes[a:b]]
+            out[a:b] = (q.reshape(b - a, K // 32, 32) * s[a:b, :, None]).reshape(-1, K)
+        nblk = N
+    else:
+        raise ValueError(fmt)
+    # independent row ranges, on a few threads (numpy releases the interpreter lock)
+    nt = os.cpu_count() or 1
+    step = max(1, -(-nblk // nt))
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(lambda a: rows(a, min(a + step, nblk)), range(0, nblk, step)))
+    return out
 
 
 _E4M3_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
+def _encode_rows(v):
+    """e4m3_encode over the rows of a 3-D block array, in row chunks on a few
+    threads (rows are independent; numpy releases the interpreter lock)."""
+    n = v.shape[0]
+    if n < 256:
+        return e4m3_encode(v)
+    out = np.empty(v.shape, dtype=np.uint8)
+    step = max(64, -(-n // (4 * (os.cpu_count() or 1))))
+
+    def work(a):
+        out[a:a + step] = e4m3_encode(v[a:a + step])
+
+    with ThreadPoolExecutor(max_workers=os.cpu_count() or 1) as ex:
+        list(ex.map(work, range(0, n, step)))
+    return out
 
 
 # ------------------------------------------------- activation quantisation
@@ -104,8 +139,8 @@ def quant_act(v, afmt, return_codes=False):
         amax = np.abs(blk).max(axis=2)
         s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
         t = (blk / s[:, :, None]).astype(np.float32)          # IEEE fp32 division
-        codes = e4m3_encode(t.astype(np.float64))
-        deq = e4m3_decode(codes) * s[:, :, None].astype(np.float64)
+        codes = _encode_rows(t.astype(np.float64))
+        deq = _E4M3_TABLE[codes] * s[:, :, None].astype(np.float64)
         out = deq.reshape(rows, K)
         if return_codes:
             return out, codes.reshape(rows, K), s
@@ -117,8 +152,8 @@ def quant_act(v, afmt, return_codes=False):
         xe = np.clip(ex - 1 - 8, -127, 127)
         xe = np.where(amax > 0, xe, 0)
         X = np.ldexp(1.0, xe)
-        codes = e4m3_encode(blk.astype(np.float64) / X[:, :, None])
-        deq = e4m3_decode(codes) * X[:, :, None]
+        codes = _encode_rows(blk.astype(np.float64) / X[:, :, None])
+        deq = _E4M3_TABLE[codes] * X[:, :, None]
         out = deq.reshape(rows, K)
         if return_codes:
             return out, codes.reshape(rows, K), (xe + 127).astype(np.uint8)
@@ -140,24 +175,37 @@ def route(x, w_router, bias, cfg):
     x: float64 [T][H]; w_router: float64 [E][H]; bias: float64 [E] or None.
     Returns dict(logits [T][E], scores [T][E], ids int32 [T][K] in descending
     score order, w float64 [T][K] = route_scale * score).
+
+    The selection compares logits: softmax is monotone, so the logit order is
+    the score order (and stays strict where a float64 score would underflow
+    to 0).  Group score = max member logit; keep the TG best groups (ties to
+    the lower group); take the K best experts of the kept groups (ties to the
+    lower id).  -inf logits are candidates like any other: they tie with each
+    other below every finite logit and get weight 0.  A token whose softmax is
+    undefined (a NaN or +inf logit) has all its candidates tie, so it takes
+    the lowest ids of the lowest groups; its weights are NaN.
     """
     x = np.asarray(x, dtype=np.float64)
     logits = x @ np.asarray(w_router, dtype=np.float64).T
     if bias is not None:
         logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
-    m = logits.max(axis=1, keepdims=True)
-    ex = np.exp(logits - m)
-    scores = ex / ex.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        m = logits.max(axis=1, keepdims=True)
+        ex = np.exp(logits - m)
+        scores = ex / ex.sum(axis=1, keepdims=True)
     T, E = scores.shape
     gsz = _group_view(cfg)
     G, TG, K = cfg.n_groups, cfg.topk_groups, cfg.topk
     ids = np.zeros((T, K), dtype=np.int32)
     w = np.zeros((T, K), dtype=np.float64)
     for t in range(T):
-        gs = scores[t].reshape(G, gsz).max(axis=1)
+        l = logits[t]
+        undefined = np.isnan(l).any() or np.isposinf(l).any()
+        key = np.full(E, -np.inf) if undefined else l
+        gs = key.reshape(G, gsz).max(axis=1)
         kept = np.argsort(-gs, kind="stable")[:TG]           # ties: lower group first
         cand = np.concatenate([np.arange(g * gsz, (g + 1) * gsz) for g in sorted(kept)])
-        order = np.lexsort((cand, -scores[t, cand]))          # by score desc, then id asc
+        order = np.lexsort((cand, -key[cand]))                # by logit desc, then id asc
         sel = cand[order[:K]]
         ids[t] = sel
         w[t] = cfg.route_scale * scores[t, sel]

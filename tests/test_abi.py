@@ -29,6 +29,11 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(moe.EXPORTS)
 
 
+def test_workspace_check_rejects_bad_arguments():
+    lib = moe._lib()
+    assert lib.moe_workspace_check(None, 1 << 20, 1, None) == EINVAL
+
+
 def cfg(**kw):
     c = moe.make_config(synth.get_config(1))
     for k, v in kw.items():
@@ -44,7 +49,7 @@ def ws_size(c, T=1):
 
 def test_status_strings():
     lib = moe._lib()
-    for s in range(6):
+    for s in range(7):
         assert lib.moe_status_string(s).decode().startswith("MOE_")
     assert b"unknown" in lib.moe_status_string(99)
 

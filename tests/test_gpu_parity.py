@@ -246,8 +246,8 @@ def test_combine():
 
 # ---------------------------------------------------------------- whole layer
 
-def _forward(cfg, inp, x=None):
-    layer = moe.Layer(cfg, inp)
+def _forward(cfg, inp, x=None, layer=None):
+    layer = moe.Layer(cfg, inp) if layer is None else layer
     out, ids, w = layer.forward(x)
     torch.cuda.synchronize()
     return out, ids, w
@@ -272,22 +272,178 @@ def test_forward_small(name, path, monkeypatch):
     assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
 
 
+def _check_dispatch(cfg, layer, r):
+    """The forward's own dispatch arrays (read from its workspace) equal the
+    oracle's, and its grouped-GEMM tile list covers every expert's segment
+    exactly once in tiles of the kernel's row count."""
+    T, K, E = cfg.tokens, cfg.topk, cfg.n_experts
+    c = layer.cfg
+    off = moe.ws_region(c, T, layer.ws, "offsets", E + 1).cpu().numpy()
+    perm = moe.ws_region(c, T, layer.ws, "perm_src", T * K).cpu().numpy()
+    inv = moe.ws_region(c, T, layer.ws, "inv_pos", T * K).cpu().numpy()
+    assert np.array_equal(off, r.offsets)
+    assert np.array_equal(perm, r.perm_src)
+    assert np.array_equal(inv, r.inv_pos)
+    bm = moe.ffn_tile_rows(c, 0)
+    n = int(moe.ws_region(c, T, layer.ws, "ntiles", 1).cpu().numpy()[0])
+    tiles = moe.ws_region(c, T, layer.ws, "tiles", 2 * n).cpu().numpy().reshape(n, 2)
+    cnt = np.diff(r.offsets)
+    want = sorted((e, m) for e in range(E) for m in range(0, int(cnt[e]), bm))
+    assert sorted(map(tuple, tiles.tolist())) == want
+
+
 @pytest.mark.parametrize("cfgname", [c.name for c in synth.CONFIGS])
-def test_forward_full_size_sampled(cfgname):
+def test_forward_full_size(cfgname):
     """Full workload sizes, default path selection (the configuration the
-    benchmark times): every token's ids exact, sampled tokens' outputs."""
+    benchmark times): every token's ids, every output row, the dispatch
+    arrays of the batched path, and three calls bitwise identical."""
     cfg = synth.get_config(cfgname)
     inp = gpu_inputs(cfg)
     say(f"[forward full] {cfgname}")
+    layer = moe.Layer(cfg, inp)
+    outs = []
+    for _ in range(3):
+        out, ids, w = layer.forward()
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy().copy(), ids.cpu().numpy().copy(), w.cpu().numpy().copy()))
+    moe.workspace_check(layer.ws)
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b), "repeated calls differ"
+    say(f"[oracle full] {cfgname}")
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    assert np.array_equal(outs[0][1], r.ids)
+    assert np.max(np.abs(outs[0][2] - r.w) / r.w) <= WTOL
+    assert rel_err(oracle.bf16_to_f64(outs[0][0].view(np.uint16)), r.out) <= TOL
+    if cfg.tokens > 4:
+        _check_dispatch(cfg, layer, r)
+
+
+# A mid-size MXFP8 layer whose H and I are multiples of 512, so its routed
+# FFN runs on the 256-row kernel, with about 300 rows per expert: every
+# expert has a full tile and a ragged tail tile.
+MX_MID = small_cfg(3, tokens=600, hidden=1024, n_experts=8, inter=512, shared_inter=512)
+
+
+def test_forward_mid_size_mx_large_tiles():
+    cfg = MX_MID
+    inp = gpu_inputs(cfg)
+    layer = moe.Layer(cfg, inp)
+    assert moe.ffn_tile_rows(layer.cfg, 0) == 256 and moe.ffn_tile_rows(layer.cfg, 1) == 256
+    say("[forward mid mx]")
+    out, ids, w = _forward(cfg, inp, layer=layer)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    cnt = np.diff(r.offsets)
+    assert ((cnt > 256) & (cnt % 256 != 0)).sum() >= 4, cnt   # full tiles plus ragged tails
+    assert np.array_equal(ids.cpu().numpy(), r.ids)
+    assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
+    _check_dispatch(cfg, layer, r)
+    out2, _, _ = _forward(cfg, inp, layer=layer)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("rows", [2000, 1793])
+def test_shared_ffn_dense_large_tiles(rows):
+    """The dense bf16 large-tile GEMM (no tile list: 8 x 28 tiles of 256 rows
+    in the down GEMM at H = 7168) with a ragged last row tile, fp32 output."""
+    cfg = synth.get_config(3).derive(tokens=rows)
+    inp = synth.make_inputs(cfg, DEV, with_experts=False)
+    shared = synth.make_experts(cfg, True, DEV)
+    c = moe.make_config(cfg)
+    ws = moe.alloc_workspace(c, rows)
+    y = torch.empty(rows, cfg.hidden, dtype=torch.float32, device=DEV)
+    say(f"[shared dense] rows={rows}")
+    moe.expert_ffn(c, 1, inp.x, None, rows, None, moe.weights_of(shared), y, ws)
+    torch.cuda.synchronize()
+    wg, wu, wd = [oracle.dequant_weight(a, None, "bf16") for a in shared.expert(0)[:3]]
+    ref = oracle.expert_ffn(oracle.bf16_to_f64(inp.x), wg, wu, wd, "none")
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
+
+
+# The DeepSeek-V2 layer at verify-sized batches: T <= 4 runs the single
+# launch (x in LDS: 40 KB at T = 4), T = 5..8 the GEMV launches with FP8
+# block-scaled weights against bf16 x.
+@pytest.mark.parametrize("T", [2, 4, 5, 8])
+def test_forward_dsv2_small_m(T):
+    cfg = synth.get_config(1).derive(tokens=T)
+    inp = gpu_inputs(cfg)
+    say(f"[forward dsv2 small-M] T={T}")
+    layer = moe.Layer(cfg, inp)
+    out, ids, w = _forward(cfg, inp, layer=layer)
+    moe.workspace_check(layer.ws)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    assert np.array_equal(ids.cpu().numpy(), r.ids)
+    assert np.max(np.abs(w.cpu().numpy() - r.w) / r.w) <= WTOL
+    assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
+    out2, _, _ = _forward(cfg, inp, layer=layer)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [5, 6, 7, 8])
+def test_forward_b128_bf16x_gemv_branch(T):
+    """FP8 block-scaled weights with bf16 activations above the single-launch
+    size: the GEMV launches (router GEMM, top-k, gate/up, down + combine)."""
+    cfg = small_cfg(1, tokens=T, hidden=640, n_experts=24, n_groups=4, topk_groups=2, topk=5, inter=384,
+                    shared_inter=512)
+    inp = gpu_inputs(cfg)
+    say(f"[forward b128 bf16-x] T={T}")
     out, ids, w = _forward(cfg, inp)
-    r = _oracle_route(cfg, inp)
-    assert np.array_equal(ids.cpu().numpy(), r["ids"])
-    T = cfg.tokens
-    tokens = sorted(set([0, T - 1] + list(np.random.default_rng(3).choice(T, min(T, 6), replace=False))))
-    say(f"[oracle tokens] {tokens}")
-    _, _, ref = oracle.forward_tokens(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared, tokens)
-    got = oracle.bf16_to_f64(out[torch.tensor(tokens, device=DEV)])
-    assert rel_err(got, ref) <= TOL
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    assert np.array_equal(ids.cpu().numpy(), r.ids)
+    assert np.max(np.abs(w.cpu().numpy() - r.w) / r.w) <= WTOL
+    assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
+
+
+@pytest.mark.parametrize("name,path", [("dsv2_like_4tok", "auto"), ("dsv2_like_4tok", "staged"),
+                                       ("b128_12exp_97tok", "auto"), ("zipf_16exp_200tok", "auto"),
+                                       ("tiny_8tok", "auto"), ("mx_4exp_160tok", "auto")])
+def test_forward_degenerate_routing(name, path, monkeypatch):
+    """A masking bias leaves fewer finite logits than slots (-inf experts fill
+    the rest, lowest id first, weight 0), and token 0 holds a NaN (no defined
+    softmax: the lowest ids, NaN weights, a NaN output row).  Every id stays
+    in range, so no kernel reads outside the weights; the other rows match."""
+    cfg = SMALL[name]
+    if path != "auto":
+        monkeypatch.setenv("MOE_FORCE_PATH", path)
+    inp = synth.make_inputs(cfg, DEV)
+    gsz = cfg.n_experts // cfg.n_groups
+    bias = torch.full((cfg.n_experts,), float("-inf"), device=DEV)
+    bias[::gsz] = 0.0                       # one finite expert per group
+    inp.bias = bias
+    inp = ensure_margin(inp)
+    inp.x[0, 5] = float("nan")
+    say(f"[degenerate] {name} {path}")
+    layer = moe.Layer(cfg, inp)
+    out, ids, w = _forward(cfg, inp, layer=layer)
+    moe.workspace_check(layer.ws)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(ids, r.ids)
+    assert list(ids[0]) == list(range(cfg.topk))   # lowest ids of the lowest groups (groups >= slots here)
+    assert np.isnan(w[0]).all() and np.isnan(r.w[0]).all()
+    assert (w[1:, cfg.topk_groups:] == 0).all()
+    o = oracle.bf16_to_f64(out)
+    assert np.isnan(o[0]).all()
+    assert rel_err(o[1:], r.out[1:]) <= TOL
+
+
+def test_single_launch_epoch_wrap():
+    """The launch tag comes from an epoch word advanced modulo 0xffffffff, so
+    consecutive launches never share a tag, also across the wrap: from epoch
+    0xfffffffe, three calls with the tokens rotated must each route their own
+    tokens (a repeated tag would hand the previous call's logits over)."""
+    cfg = SMALL["dsv2_like_4tok"]
+    inp = gpu_inputs(cfg)
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    layer = moe.Layer(cfg, inp)
+    layer.ws[4:8].view(torch.int32).fill_(-2)    # epoch word = 0xfffffffe
+    for k, want_epoch in enumerate((0, 1, 2)):
+        order = [(k + i) % 4 for i in range(4)]
+        out, ids, w = _forward(cfg, inp, inp.x[order].contiguous(), layer=layer)
+        assert np.array_equal(ids.cpu().numpy(), r.ids[order])
+        assert rel_err(oracle.bf16_to_f64(out), r.out[order]) <= TOL
+        q = _queue_words(layer)
+        assert q[0] == 0 and q[1] == want_epoch
 
 
 def test_forward_is_bitwise_deterministic():

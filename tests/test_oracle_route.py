@@ -92,3 +92,50 @@ def test_margin_detects_a_near_tie():
     assert oracle.route_margins(l, cfg)[0] < 1e-3
     l2 = np.array([[0.1, 2.0, 1.5, -1.0, 0.3, 1.9, 3.0, -2.0]])
     assert abs(oracle.route_margins(l2, cfg)[0] - 0.1) < 1e-12   # group gap 2.0 vs 1.9
+
+
+def test_neg_inf_logits_tie_below_finite_ones():
+    """-inf logits (a masking bias) are candidates that tie with each other
+    below every finite logit; they get weight 0.  Hand-worked: groups of 4,
+    keep 1 group, top 3.  g0 holds one finite logit (1.0 at e2), g1 one (2.0
+    at e5), so g1 is kept; e5 first, then the -inf members e4, e6 by id."""
+    b = np.array([-np.inf, -np.inf, 1.0, -np.inf, -np.inf, 2.0, -np.inf, -np.inf])
+    r = oracle.route(np.zeros((1, 8)), np.eye(8), b, _Cfg(8, 2, 1, 3, 2.0))   # logits = bias
+    assert list(r["ids"][0]) == [5, 4, 6]
+    assert abs(r["w"][0, 0] - 2.0 * math.exp(2.0) / (math.exp(1.0) + math.exp(2.0))) < 1e-15
+    assert r["w"][0, 1] == 0.0 and r["w"][0, 2] == 0.0
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf])
+def test_undefined_softmax_routes_to_lowest_ids(bad):
+    """A NaN or +inf logit leaves the softmax undefined: every candidate ties,
+    so the token takes the lowest ids of the lowest kept groups (g0, g1 of 4
+    groups of 2 with 2 kept; 3 slots: e0, e1, e2) and NaN weights."""
+    l = np.array([0.1, 2.0, 1.5, -1.0, 0.3, 1.9, 3.0, -2.0])
+    r = oracle.route(np.eye(8)[[5]] * 0, np.eye(8), l + np.where(np.arange(8) == 5, bad, 0.0), _Cfg(8, 4, 2, 3, 2.0))
+    assert list(r["ids"][0]) == [0, 1, 2]
+    assert np.isnan(r["w"][0]).all()
+    r = oracle.route(np.zeros((1, 8)), np.eye(8), l, _Cfg(8, 4, 2, 3, 2.0))
+    assert list(r["ids"][0]) == [6, 1, 0]   # without the bad logit: the hand example
+
+
+def test_all_neg_inf_token():
+    r = oracle.route(np.zeros((1, 8)), np.eye(8), np.full(8, -np.inf), _Cfg(8, 4, 2, 3))
+    assert list(r["ids"][0]) == [0, 1, 2]
+    assert np.isnan(r["w"][0]).all()
+
+
+def test_zipf_workload_skew_in_band():
+    """The skewed 4,096-token workload: a router bias b[e] = -1.2 ln(rank_e)
+    stands in for trained-router popularity (Zipf, s = 1.2).  Its realised
+    load, routed by the oracle, has max/mean in [15, 160/6]: the hottest
+    expert near 20x the mean, capped by each token taking 6 distinct experts."""
+    cfg = synth.get_config("dsv2_4096tok_zipf")
+    inp = ensure_margin(synth.make_inputs(cfg, with_experts=False))
+    r = oracle.route(oracle.bf16_to_f64(inp.x), oracle.bf16_to_f64(inp.w_router),
+                     inp.bias.double().numpy(), cfg)
+    cnt = np.bincount(r["ids"].ravel(), minlength=cfg.n_experts)
+    ratio = cnt.max() / cnt.mean()
+    assert 15.0 <= ratio <= 160 / 6, ratio
+    # groups still bind: every token's experts come from at most 3 groups
+    assert max(len(set(int(e) // 20 for e in row)) for row in r["ids"]) <= 3
