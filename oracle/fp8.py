@@ -41,7 +41,8 @@ def e4m3_encode(values):
     # normal range: a = 2^E * f, f in [1, 2)
     f, ex = np.frexp(np.where(sub, 1.0, a))                # a = f' * 2^ex, f' in [0.5, 1)
     E = ex - 1
-    mant = np.rint((f * 2.0 - 1.0) * 8.0).astype(np.int64)  # 0..8, ties to even
+    with np.errstate(invalid="ignore"):                    # NaN inputs give an arbitrary code
+        mant = np.rint((f * 2.0 - 1.0) * 8.0).astype(np.int64)  # 0..8, ties to even
     E = np.where(mant == 8, E + 1, E)
     mant = np.where(mant == 8, 0, mant)
     ncode = ((E + 7) << 3) | mant

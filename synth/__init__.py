@@ -9,4 +9,4 @@ DSV2-236B-MegaKernel README ("Layout": the block-FP8 quantiser) quantises a
 checkpoint offline before any forward pass.
 """
 from .configs import CONFIGS, LayerConfig, get_config  # noqa: F401
-from .generate import LayerInputs, ExpertWeights, make_inputs, redraw_tokens, draw_tokens  # noqa: F401
+from .generate import LayerInputs, ExpertWeights, make_inputs, make_experts, redraw_tokens, draw_tokens  # noqa: F401
