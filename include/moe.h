@@ -216,6 +216,25 @@ moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_
                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, paths and results as moe_forward; the
+ * workspace is a 32 MiB device array inside the library, one per GPU,
+ * resolved on the first call on a device (whose counter block that call
+ * clears on `stream`) and held until the process ends.  No call allocates
+ * memory or creates a stream.  Every call on a GPU uses that GPU's one
+ * array: calls that overlap on one GPU (several streams or threads) race,
+ * so order them on one stream.  The shared expert always runs in order on
+ * `stream`.  MOE_EWORKSPACE when the call needs more than 32 MiB of
+ * workspace (moe_workspace_size for T tokens); MOE_EHIP if the array cannot
+ * be resolved.  A bounded wait of the single launch that gives up shows as
+ * NaN rows of `out` (the array's error word is not exposed). */
+moe_status moe_forward_noalloc(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
+                               const uint16_t* w_router, const float* bias,
+                               const moe_ffn_weights* routed /*host struct*/,
+                               const moe_ffn_weights* shared /*host struct or NULL*/, uint16_t* out,
+                               int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
+
 /* Reports the sticky error word of a workspace used by moe_forward's
  * single-launch path: MOE_EWAIT if a bounded wait of an earlier call gave up
  * (its output rows are NaN), else MOE_OK.  clear != 0 resets the word.

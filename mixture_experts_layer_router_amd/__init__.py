@@ -63,6 +63,8 @@ def _lib():
             "moe_forward": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
             "moe_workspace_check": (_i32, [_vp, _sz, _i32, _vp]),
+            "moe_forward_noalloc": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp,
+                                           _vp, _vp]),
             "moe_debug_ws_offset": (_i32, [P(Config), _i32, _i32, P(_sz)]),
             "moe_debug_ffn_tile_rows": (_i32, [P(Config), _i32]),
             "moe_debug_e4m3_decode": (_i32, [_vp, _vp, _i32, _vp]),
@@ -79,7 +81,7 @@ def _lib():
 
 
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_workspace_check", "moe_debug_ws_offset",
+           "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_workspace_check", "moe_debug_ws_offset",
            "moe_debug_ffn_tile_rows", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
            "moe_debug_trace_count", "moe_debug_trace_name")
 
@@ -179,6 +181,13 @@ def ws_region(cfg, max_tokens, ws, name, count):
 
 def ffn_tile_rows(cfg, which):
     return _lib().moe_debug_ffn_tile_rows(ctypes.byref(cfg), int(which))
+
+
+def forward_noalloc(cfg, x, w_router, bias, routed, shared, out, ids, w, stream=None):
+    """moe_forward on the library's own per-GPU device array (no workspace)."""
+    _check(_lib().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), x.shape[0], _ptr(w_router), _ptr(bias),
+                                      ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
+                                      _ptr(out), _ptr(ids), _ptr(w), _stream(stream)), "moe_forward_noalloc")
 
 
 def e4m3_decode(codes, out, stream=None):

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "../../include/moe.h"
+#include "common.h"
 #include "kernels.h"
 
 using namespace moe;
@@ -339,6 +340,326 @@ moe_status shared_ffn(const moe_config* cfg, const uint16_t* x, int T, const moe
                   at<void>(ws, L.hshs), *ysh, false, s);
 }
 
+// moe_forward on a given workspace.  side_ok: a shared expert too small to
+// fill the chip may run on the side stream (created on first use); false
+// keeps every launch on the caller's stream.
+moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
+                        const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared, uint16_t* out,
+                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                        bool side_ok) {
+  hipStream_t s_ = stream;
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !routed || !out || !ws) return MOE_EINVAL;
+  const bool has_shared = cfg->shared_inter > 0;
+  if (has_shared && !shared) return MOE_EINVAL;
+  if ((st = check_weights(routed, cfg->routed_wfmt)) != MOE_OK) return st;
+  if (has_shared && (st = check_weights(shared, cfg->shared_wfmt)) != MOE_OK) return st;
+  for (const void* p : {(const void*)x, (const void*)w_router, (const void*)out, (const void*)ws})
+    if (!aligned16(p)) return MOE_EALIGN;
+  const Ws L = plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+
+  const int H = cfg->hidden, K = cfg->topk, E = cfg->n_experts, TK = T * K;
+  const int raf = cfg->routed_afmt, saf = cfg->shared_afmt;
+  int* ids = topk_ids_out ? topk_ids_out : at<int>(ws, L.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  const int fp = forced_path();
+  const bool pairs_ok = gemm_pair(cfg->routed_wfmt, raf) && (!has_shared || gemm_pair(cfg->shared_wfmt, saf));
+  if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
+  const bool gemv = fp == 1 || fp == 3 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
+
+  if (gemv && T <= kRouteGemvMaxT && fp != 3 && raf == A_NONE && size_t(T) * H * 2 <= size_t(kFusedXLdsMax) &&
+      H % 8 == 0 && (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt))) {
+    // small T, bf16 activations: the whole layer in one persistent launch
+    FusedDecodeParams fp_{};
+    DecodeParams& dp = fp_.d;
+    dp.x = x;
+    dp.T = T;
+    dp.H = H;
+    dp.wr = w_router;
+    dp.bias = bias;
+    dp.rp = route_params(cfg);
+    dp.logits = at<float>(ws, L.logits);
+    dp.ids = ids;
+    dp.w = w;
+    dp.swfmt = has_shared ? cfg->shared_wfmt : W_BF16;
+    if (has_shared) {
+      dp.xs = x;
+      dp.sg = shared->gate; dp.su = shared->up; dp.sgs = shared->gate_s; dp.sus = shared->up_s;
+      dp.sd = shared->down; dp.sds = shared->down_s;
+      dp.Is = cfg->shared_inter;
+      dp.hs = at<float>(ws, L.hsh);
+    }
+    fp_.wfmt = cfg->routed_wfmt;
+    fp_.I = cfg->inter;
+    fp_.g = routed->gate; fp_.u = routed->up; fp_.gs = routed->gate_s; fp_.us = routed->up_s;
+    fp_.dn = routed->down; fp_.dns = routed->down_s;
+    fp_.h = at<float>(ws, L.h);
+    fp_.out = out;
+    fp_.ctr = at<unsigned>(ws, L.counter);
+    LAUNCH("decode_fused", launch_fused_decode(fp_, stream));
+    return MOE_OK;
+  }
+
+  if (gemv && T <= kRouteGemvMaxT) {
+    // small T: router || shared gate/up, then top-k || shared down, then the
+    // routed experts; the kernel boundaries are the only synchronisation
+    const void* xs = x;
+    bool xs32 = false;
+    if (has_shared && saf != A_NONE) {
+      LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
+      xs = at<float>(ws, L.xs2);
+      xs32 = true;
+    }
+    DecodeParams dp{};
+    dp.x = x;
+    dp.T = T;
+    dp.H = H;
+    dp.wr = w_router;
+    dp.bias = bias;
+    dp.rp = route_params(cfg);
+    dp.logits = at<float>(ws, L.logits);
+    dp.ids = ids;
+    dp.w = w;
+    dp.swfmt = has_shared ? cfg->shared_wfmt : W_BF16;
+    if (has_shared) {
+      dp.xs = xs;
+      dp.xs_f32 = xs32;
+      dp.sg = shared->gate; dp.su = shared->up; dp.sgs = shared->gate_s; dp.sus = shared->up_s;
+      dp.sd = shared->down; dp.sds = shared->down_s;
+      dp.Is = cfg->shared_inter;
+      dp.hs = at<float>(ws, L.hsh);
+      dp.ysh = at<float>(ws, L.ysh);
+    }
+    LAUNCH("decode_router_shared_up", launch_decode_stage1(dp, stream));
+    if (has_shared && saf != A_NONE)
+      LAUNCH("quant_rows", launch_quant_rows(dp.hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, dp.hs, stream));
+    LAUNCH("decode_topk_shared_down", launch_decode_stage2(dp, stream));
+    const void* xr = x;
+    bool xr32 = false;
+    if (raf != A_NONE) {
+      if (saf == raf && has_shared) {
+        xr = xs;
+      } else {
+        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
+        xr = at<float>(ws, L.xq);
+      }
+      xr32 = true;
+    }
+    float* h = at<float>(ws, L.h);
+    GemvUpParams u{};
+    u.wfmt = cfg->routed_wfmt;
+    u.swfmt = cfg->routed_wfmt;
+    u.x = xr;
+    u.x_f32 = xr32;
+    u.T = T;
+    u.H = H;
+    u.ids = ids;
+    u.K = K;
+    u.g = routed->gate; u.u = routed->up; u.gs = routed->gate_s; u.us = routed->up_s;
+    u.I = cfg->inter;
+    u.h = h;
+    u.E = E;
+    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
+    if (raf != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
+    GemvDownParams d{};
+    d.wfmt = cfg->routed_wfmt;
+    d.swfmt = cfg->routed_wfmt;
+    d.T = T;
+    d.H = H;
+    d.K = K;
+    d.I = cfg->inter;
+    d.ids = ids;
+    d.w = w;
+    d.h = h;
+    d.d = routed->down; d.ds = routed->down_s;
+    d.out = out;
+    d.E = E;
+    d.ys_add = has_shared ? dp.ysh : nullptr;
+    LAUNCH("gemv_down_combine", launch_gemv_down(d, stream));
+    return MOE_OK;
+  }
+
+  // batched path, shared expert whose gate/up grid fills at most half the
+  // CUs (128-row tiles, 128 output columns each): it forks onto the side
+  // stream before the routing.  A larger one stays in order on the caller's
+  // stream: beside the routed GEMMs it measured slower (their tiles take the
+  // same CUs).
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  SideJoin joiner;  // declared after the lock: it joins before the lock is released
+  float* ysh = nullptr;
+  if (!gemv && has_shared && side_ok &&
+      long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128) {
+    side_lock.lock();
+    side = side_stream(stream);
+    if (side) {
+      HIP_TRY(hipEventRecord(side->fork, stream));
+      HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
+      joiner.side = side;
+      joiner.caller = stream;
+      if ((st = shared_ffn(cfg, x, T, shared, ws, L, &ysh, side->s)) != MOE_OK) return st;
+    }
+  }
+
+  if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
+
+  if (gemv) {  // T > kRouteGemvMaxT on the GEMV path: routed + shared gate/up in one launch
+    const void* xr = x;
+    bool xr32 = false;
+    if (raf != A_NONE) {
+      LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
+      xr = at<float>(ws, L.xq);
+      xr32 = true;
+    }
+    const void* xs = x;
+    bool xs32 = false;
+    if (has_shared && saf != A_NONE) {
+      if (saf == raf) {
+        xs = xr;
+      } else {
+        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
+        xs = at<float>(ws, L.xs2);
+      }
+      xs32 = true;
+    }
+    float* h = at<float>(ws, L.h);
+    float* hs = has_shared ? at<float>(ws, L.hsh) : nullptr;
+    GemvUpParams u{};
+    u.wfmt = cfg->routed_wfmt;
+    u.swfmt = has_shared ? cfg->shared_wfmt : cfg->routed_wfmt;
+    u.x = xr;
+    u.x_f32 = xr32;
+    u.T = T;
+    u.H = H;
+    u.ids = ids;
+    u.K = K;
+    u.g = routed->gate; u.u = routed->up; u.gs = routed->gate_s; u.us = routed->up_s;
+    u.I = cfg->inter;
+    u.h = h;
+    if (has_shared) {
+      u.sg = shared->gate; u.su = shared->up; u.sgs = shared->gate_s; u.sus = shared->up_s;
+      u.Is = cfg->shared_inter;
+      u.hs = hs;
+      u.xs = xs;
+      u.xs_f32 = xs32;
+    }
+    u.E = E;
+    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
+    if (raf != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
+    if (has_shared && saf != A_NONE)
+      LAUNCH("quant_rows", launch_quant_rows(hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, hs, stream));
+    GemvDownParams d{};
+    d.wfmt = cfg->routed_wfmt;
+    d.swfmt = u.swfmt;
+    d.T = T;
+    d.H = H;
+    d.K = K;
+    d.I = cfg->inter;
+    d.Is = cfg->shared_inter;
+    d.ids = ids;
+    d.w = w;
+    d.h = h;
+    d.hs = hs;
+    d.d = routed->down; d.ds = routed->down_s;
+    if (has_shared) { d.sd = shared->down; d.sds = shared->down_s; }
+    d.out = out;
+    d.E = E;
+    LAUNCH("gemv_down_combine", launch_gemv_down(d, stream));
+    return MOE_OK;
+  }
+
+  // batched path
+  int* off = at<int>(ws, L.offsets);
+  int* perm = at<int>(ws, L.perm);
+  int* inv = at<int>(ws, L.inv);
+  int* tiles = at<int>(ws, L.tiles);
+  int* ntiles = at<int>(ws, L.ntiles);
+  const int rbm = ffn_tile_rows(cfg->routed_wfmt, H, cfg->inter);
+  LAUNCH("permute", launch_permute(ids, TK, E, at<int>(ws, L.hist), off, perm, inv, tiles, ntiles, rbm, stream));
+  const void* xa = x;
+  const void* xas = nullptr;
+  if (raf != A_NONE) {
+    LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
+                              stream));
+    xa = at<void>(ws, L.xq);
+    xas = at<void>(ws, L.xqs);
+  }
+  if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, rbm), rbm, routed,
+                     at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
+    return st;
+  if (has_shared && !side) {  // in order on the caller's stream
+    const void* xs = x;
+    const void* xss = nullptr;
+    if (saf != A_NONE) {
+      if (saf == raf) {
+        xs = xa;
+        xss = xas;
+      } else {
+        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
+                                  nullptr, stream));
+        xs = at<void>(ws, L.xs2);
+        xss = at<void>(ws, L.xs2s);
+      }
+    }
+    ysh = at<float>(ws, L.ysh);
+    if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
+                       ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
+                       at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
+      return st;
+  }
+  HIP_TRY(joiner.join());
+  LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
+  return MOE_OK;
+}
+
+// Workspace of moe_forward_noalloc: a file-scope device array, one copy per
+// GPU, held from the library's first use on that GPU until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: host
+// code uses only the address hipGetSymbolAddress gives for the current
+// device (g_scratch), never the name.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static_assert(kScratchBytes >= size_t(kFusedCtrBytes), "scratch holds the counter block");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchDev {
+  void* ptr = nullptr;
+};
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[64];
+
+// zero-fills n 16-byte words at p (a kernel, not a memset: callers may be
+// under graph capture)
+__global__ void zero_words_kernel(i32x4* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = i32x4{0, 0, 0, 0};
+}
+
+// The scratch address on the device of `stream`, set up on first use: the
+// symbol is resolved with that device current and its counter block (which
+// the single-launch path needs zero before its first launch) is cleared on
+// `stream`.  Null if the device cannot be had.
+void* scratch_for(hipStream_t stream) {
+  int dev = 0, cur = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchDev& sd = g_scratch[dev];
+  if (sd.ptr) return sd.ptr;
+  if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  (void)hipSetDevice(cur);
+  if (e != hipSuccess || !p) return nullptr;
+  const int n = kFusedCtrBytes / 16;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<i32x4*>(p), n);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  sd.ptr = p;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -520,273 +841,22 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
 moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
                        const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared, uint16_t* out,
                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  hipStream_t s_ = stream;
+  return forward_impl(cfg, x, T, w_router, bias, routed, shared, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream,
+                      true);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
+                               const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared,
+                               uint16_t* out, int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream) {
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  if (!x || !w_router || !routed || !out || !ws) return MOE_EINVAL;
-  const bool has_shared = cfg->shared_inter > 0;
-  if (has_shared && !shared) return MOE_EINVAL;
-  if ((st = check_weights(routed, cfg->routed_wfmt)) != MOE_OK) return st;
-  if (has_shared && (st = check_weights(shared, cfg->shared_wfmt)) != MOE_OK) return st;
-  for (const void* p : {(const void*)x, (const void*)w_router, (const void*)out, (const void*)ws})
-    if (!aligned16(p)) return MOE_EALIGN;
-  const Ws L = plan(cfg, T);
-  if (ws_bytes < L.total) return MOE_EWORKSPACE;
-
-  const int H = cfg->hidden, K = cfg->topk, E = cfg->n_experts, TK = T * K;
-  const int raf = cfg->routed_afmt, saf = cfg->shared_afmt;
-  int* ids = topk_ids_out ? topk_ids_out : at<int>(ws, L.ids);
-  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
-  const int fp = forced_path();
-  const bool pairs_ok = gemm_pair(cfg->routed_wfmt, raf) && (!has_shared || gemm_pair(cfg->shared_wfmt, saf));
-  if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
-  const bool gemv = fp == 1 || fp == 3 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
-
-  if (gemv && T <= kRouteGemvMaxT && fp != 3 && raf == A_NONE && size_t(T) * H * 2 <= size_t(kFusedXLdsMax) &&
-      H % 8 == 0 && (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt))) {
-    // small T, bf16 activations: the whole layer in one persistent launch
-    FusedDecodeParams fp_{};
-    DecodeParams& dp = fp_.d;
-    dp.x = x;
-    dp.T = T;
-    dp.H = H;
-    dp.wr = w_router;
-    dp.bias = bias;
-    dp.rp = route_params(cfg);
-    dp.logits = at<float>(ws, L.logits);
-    dp.ids = ids;
-    dp.w = w;
-    dp.swfmt = has_shared ? cfg->shared_wfmt : W_BF16;
-    if (has_shared) {
-      dp.xs = x;
-      dp.sg = shared->gate; dp.su = shared->up; dp.sgs = shared->gate_s; dp.sus = shared->up_s;
-      dp.sd = shared->down; dp.sds = shared->down_s;
-      dp.Is = cfg->shared_inter;
-      dp.hs = at<float>(ws, L.hsh);
-    }
-    fp_.wfmt = cfg->routed_wfmt;
-    fp_.I = cfg->inter;
-    fp_.g = routed->gate; fp_.u = routed->up; fp_.gs = routed->gate_s; fp_.us = routed->up_s;
-    fp_.dn = routed->down; fp_.dns = routed->down_s;
-    fp_.h = at<float>(ws, L.h);
-    fp_.out = out;
-    fp_.ctr = at<unsigned>(ws, L.counter);
-    LAUNCH("decode_fused", launch_fused_decode(fp_, stream));
-    return MOE_OK;
-  }
-
-  if (gemv && T <= kRouteGemvMaxT) {
-    // small T: router || shared gate/up, then top-k || shared down, then the
-    // routed experts; the kernel boundaries are the only synchronisation
-    const void* xs = x;
-    bool xs32 = false;
-    if (has_shared && saf != A_NONE) {
-      LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
-      xs = at<float>(ws, L.xs2);
-      xs32 = true;
-    }
-    DecodeParams dp{};
-    dp.x = x;
-    dp.T = T;
-    dp.H = H;
-    dp.wr = w_router;
-    dp.bias = bias;
-    dp.rp = route_params(cfg);
-    dp.logits = at<float>(ws, L.logits);
-    dp.ids = ids;
-    dp.w = w;
-    dp.swfmt = has_shared ? cfg->shared_wfmt : W_BF16;
-    if (has_shared) {
-      dp.xs = xs;
-      dp.xs_f32 = xs32;
-      dp.sg = shared->gate; dp.su = shared->up; dp.sgs = shared->gate_s; dp.sus = shared->up_s;
-      dp.sd = shared->down; dp.sds = shared->down_s;
-      dp.Is = cfg->shared_inter;
-      dp.hs = at<float>(ws, L.hsh);
-      dp.ysh = at<float>(ws, L.ysh);
-    }
-    LAUNCH("decode_router_shared_up", launch_decode_stage1(dp, stream));
-    if (has_shared && saf != A_NONE)
-      LAUNCH("quant_rows", launch_quant_rows(dp.hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, dp.hs, stream));
-    LAUNCH("decode_topk_shared_down", launch_decode_stage2(dp, stream));
-    const void* xr = x;
-    bool xr32 = false;
-    if (raf != A_NONE) {
-      if (saf == raf && has_shared) {
-        xr = xs;
-      } else {
-        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
-        xr = at<float>(ws, L.xq);
-      }
-      xr32 = true;
-    }
-    float* h = at<float>(ws, L.h);
-    GemvUpParams u{};
-    u.wfmt = cfg->routed_wfmt;
-    u.swfmt = cfg->routed_wfmt;
-    u.x = xr;
-    u.x_f32 = xr32;
-    u.T = T;
-    u.H = H;
-    u.ids = ids;
-    u.K = K;
-    u.g = routed->gate; u.u = routed->up; u.gs = routed->gate_s; u.us = routed->up_s;
-    u.I = cfg->inter;
-    u.h = h;
-    u.E = E;
-    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
-    if (raf != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
-    GemvDownParams d{};
-    d.wfmt = cfg->routed_wfmt;
-    d.swfmt = cfg->routed_wfmt;
-    d.T = T;
-    d.H = H;
-    d.K = K;
-    d.I = cfg->inter;
-    d.ids = ids;
-    d.w = w;
-    d.h = h;
-    d.d = routed->down; d.ds = routed->down_s;
-    d.out = out;
-    d.E = E;
-    d.ys_add = has_shared ? dp.ysh : nullptr;
-    LAUNCH("gemv_down_combine", launch_gemv_down(d, stream));
-    return MOE_OK;
-  }
-
-  // batched path, shared expert whose gate/up grid fills at most half the
-  // CUs (128-row tiles, 128 output columns each): it forks onto the side
-  // stream before the routing.  A larger one stays in order on the caller's
-  // stream: beside the routed GEMMs it measured slower (their tiles take the
-  // same CUs).
-  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  SideStream* side = nullptr;
-  SideJoin joiner;  // declared after the lock: it joins before the lock is released
-  float* ysh = nullptr;
-  if (!gemv && has_shared &&
-      long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128) {
-    side_lock.lock();
-    side = side_stream(stream);
-    if (side) {
-      HIP_TRY(hipEventRecord(side->fork, stream));
-      HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
-      joiner.side = side;
-      joiner.caller = stream;
-      if ((st = shared_ffn(cfg, x, T, shared, ws, L, &ysh, side->s)) != MOE_OK) return st;
-    }
-  }
-
-  if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
-
-  if (gemv) {  // T > kRouteGemvMaxT on the GEMV path: routed + shared gate/up in one launch
-    const void* xr = x;
-    bool xr32 = false;
-    if (raf != A_NONE) {
-      LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, nullptr, nullptr, at<float>(ws, L.xq), stream));
-      xr = at<float>(ws, L.xq);
-      xr32 = true;
-    }
-    const void* xs = x;
-    bool xs32 = false;
-    if (has_shared && saf != A_NONE) {
-      if (saf == raf) {
-        xs = xr;
-      } else {
-        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, nullptr, nullptr, at<float>(ws, L.xs2), stream));
-        xs = at<float>(ws, L.xs2);
-      }
-      xs32 = true;
-    }
-    float* h = at<float>(ws, L.h);
-    float* hs = has_shared ? at<float>(ws, L.hsh) : nullptr;
-    GemvUpParams u{};
-    u.wfmt = cfg->routed_wfmt;
-    u.swfmt = has_shared ? cfg->shared_wfmt : cfg->routed_wfmt;
-    u.x = xr;
-    u.x_f32 = xr32;
-    u.T = T;
-    u.H = H;
-    u.ids = ids;
-    u.K = K;
-    u.g = routed->gate; u.u = routed->up; u.gs = routed->gate_s; u.us = routed->up_s;
-    u.I = cfg->inter;
-    u.h = h;
-    if (has_shared) {
-      u.sg = shared->gate; u.su = shared->up; u.sgs = shared->gate_s; u.sus = shared->up_s;
-      u.Is = cfg->shared_inter;
-      u.hs = hs;
-      u.xs = xs;
-      u.xs_f32 = xs32;
-    }
-    u.E = E;
-    LAUNCH("gemv_gate_up", launch_gemv_gate_up(u, stream));
-    if (raf != A_NONE) LAUNCH("quant_rows", launch_quant_rows(h, true, TK, cfg->inter, nullptr, 1, raf, nullptr, nullptr, h, stream));
-    if (has_shared && saf != A_NONE)
-      LAUNCH("quant_rows", launch_quant_rows(hs, true, T, cfg->shared_inter, nullptr, 1, saf, nullptr, nullptr, hs, stream));
-    GemvDownParams d{};
-    d.wfmt = cfg->routed_wfmt;
-    d.swfmt = u.swfmt;
-    d.T = T;
-    d.H = H;
-    d.K = K;
-    d.I = cfg->inter;
-    d.Is = cfg->shared_inter;
-    d.ids = ids;
-    d.w = w;
-    d.h = h;
-    d.hs = hs;
-    d.d = routed->down; d.ds = routed->down_s;
-    if (has_shared) { d.sd = shared->down; d.sds = shared->down_s; }
-    d.out = out;
-    d.E = E;
-    LAUNCH("gemv_down_combine", launch_gemv_down(d, stream));
-    return MOE_OK;
-  }
-
-  // batched path
-  int* off = at<int>(ws, L.offsets);
-  int* perm = at<int>(ws, L.perm);
-  int* inv = at<int>(ws, L.inv);
-  int* tiles = at<int>(ws, L.tiles);
-  int* ntiles = at<int>(ws, L.ntiles);
-  const int rbm = ffn_tile_rows(cfg->routed_wfmt, H, cfg->inter);
-  LAUNCH("permute", launch_permute(ids, TK, E, at<int>(ws, L.hist), off, perm, inv, tiles, ntiles, rbm, stream));
-  const void* xa = x;
-  const void* xas = nullptr;
-  if (raf != A_NONE) {
-    LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
-                              stream));
-    xa = at<void>(ws, L.xq);
-    xas = at<void>(ws, L.xqs);
-  }
-  if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, rbm), rbm, routed,
-                     at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
-    return st;
-  if (has_shared && !side) {  // in order on the caller's stream
-    const void* xs = x;
-    const void* xss = nullptr;
-    if (saf != A_NONE) {
-      if (saf == raf) {
-        xs = xa;
-        xss = xas;
-      } else {
-        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
-                                  nullptr, stream));
-        xs = at<void>(ws, L.xs2);
-        xss = at<void>(ws, L.xs2s);
-      }
-    }
-    ysh = at<float>(ws, L.ysh);
-    if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
-                       ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
-                       at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
-      return st;
-  }
-  HIP_TRY(joiner.join());
-  LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
-  return MOE_OK;
+  if (plan(cfg, T).total > kScratchBytes) return MOE_EWORKSPACE;
+  void* ws = scratch_for(stream);
+  if (!ws) return MOE_EHIP;
+  return forward_impl(cfg, x, T, w_router, bias, routed, shared, out, topk_ids_out, topk_w_out, ws, kScratchBytes,
+                      stream, false);
 }
 
 moe_status moe_debug_ws_offset(const moe_config* cfg, int32_t max_tokens, int32_t region, size_t* offset) {
