@@ -364,7 +364,7 @@ def small_m(moe, synth, torch, tokens=(2, 4, 8), replicas=8):
         b = statistics.mean(nbytes)
         res.append({"tokens": T, "us_per_layer": round(ms * 1e3, 2), "algorithmic_bytes": int(b),
                     "hbm_GBps": round(b / (ms * 1e-3) / 1e9, 1),
-                    "path": "single launch" if T <= 4 else "staged GEMV launches"})
+                    "path": "single launch" if T <= 8 else "GEMV launches"})
         del layers, reps
         torch.cuda.empty_cache()
     return res

@@ -28,7 +28,7 @@
  * - The caller owns all memory.  The library never allocates.  Calls that
  *   take a workspace need `ws_bytes` >= moe_workspace_size(); the workspace
  *   must be zero-filled once before its first use (torch.zeros is enough):
- *   its first 32 KiB hold the work queues, counters, a launch epoch and
+ *   its first 48 KiB hold the work queues, counters, a launch epoch and
  *   tagged router logits of moe_forward's single-launch path; every call
  *   leaves the queues and counters zero again and advances the epoch.  Calls sharing
  *   one workspace must be ordered on one stream; overlapping calls on one
@@ -136,6 +136,16 @@ const char* moe_status_string(int32_t status);
 moe_status moe_workspace_size(const moe_config* cfg /*host*/, int32_t max_tokens,
                               size_t* bytes /*host*/);
 
+/* Stage M of the DSV2-236B-MegaKernel README flowchart (the post-attention
+ * RMSNorm with weight gamma4, just before the router GEMV): gamma bf16 [H]
+ * (device), eps >= 0.  The layer input becomes
+ *   x = bf16( fl32( fl32(h * gamma) * r ) ),  r = fl32( 1 / sqrt(mean(h^2) + eps) )
+ * per row, with mean(h^2) in float64 and each rounding to nearest even. */
+typedef struct {
+  const uint16_t* gamma;
+  float eps;
+} moe_norm;
+
 /* Stages N + O: router GEMV and group-limited greedy top-k.
  * x bf16 [T][H]; w_router bf16 [E][H]; bias fp32 [E] or NULL (added to the
  * logits before the softmax).  Outputs topk_ids int32 [T][K] in descending
@@ -166,6 +176,24 @@ moe_status moe_permute(const moe_config* cfg /*host*/, const int32_t* topk_ids, 
                        int32_t* inv_pos, void* x_perm, void* x_perm_scale, void* ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Stages M (optional) + N + O and the dispatch in one call, the router
+ * emitting the layout the experts need ("From 35 to 873 tokens/s", Rounds
+ * 12-15; Mixture-of-Kittens, Figure 1): the norm, the router, the top-k, the
+ * routed experts' input in their activation format and the per-block expert
+ * counts in one launch, then the stable scatter.  Any T >= 1.
+ *   h bf16 [T][H]: the pre-norm rows when norm != NULL, else x itself.
+ *   Outputs as moe_route and moe_permute (topk_ids, topk_w, expert_offsets,
+ *   perm_src, inv_pos), plus, each optional (NULL to skip):
+ *   x_out bf16 [T][H]: x (normalised when norm != NULL);
+ *   xq u8 [T][H] + xq_scale: x quantised in the routed activation format
+ *   (per token, not gathered: row perm_src[pos]/K feeds permuted row pos);
+ *   MOE_EINVAL if xq is given and that format is MOE_A_NONE. */
+moe_status moe_route_dispatch(const moe_config* cfg /*host*/, const uint16_t* h, int32_t T,
+                              const moe_norm* norm /*host struct or NULL*/, const uint16_t* w_router,
+                              const float* bias, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                              int32_t* perm_src, int32_t* inv_pos, uint16_t* x_out, void* xq, void* xq_scale,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Stages P1+P2 (which = 0, routed) or Q1+Q2 (which = 1, shared): the SwiGLU
  * FFN y = (SiLU(x.Wg^T) * (x.Wu^T)).Wd^T on `rows` rows.
  *   x: bf16 [rows][H] when x_scale is NULL (quantised here per the afmt),
@@ -192,8 +220,8 @@ moe_status moe_combine(const moe_config* cfg /*host*/, const float* y_perm, cons
  * out bf16 [T][H].  topk_ids_out int32 [T][K] and topk_w_out fp32 [T][K]
  * may be NULL.  Numerics depend only on cfg: every path honours the same
  * activation format.
- * Paths: T <= 4 with both activation formats MOE_A_NONE and one weight
- * format for routed and shared experts runs as ONE
+ * Paths: T <= 8 with both activation formats MOE_A_NONE, T * H * 2 <= 80 KiB
+ * and one weight format for routed and shared experts runs as ONE
  * persistent launch (the DSV2-236B-MegaKernel README's single-launch idea,
  * "What runs inside the single launch"): workgroups take router rows,
  * shared gate/up, routed gate/up and down+combine items in that order from
@@ -206,9 +234,9 @@ moe_status moe_combine(const moe_config* cfg /*host*/, const float* y_perm, cons
  * the router rows, and each of 32 queues needs a resident server); the
  * launch asks for the device's full resident capacity, so only a kernel on
  * another stream that holds most of the CUs for longer than the wait bound
- * can make a wait give up.  Other T <= 4 cases run in four to six launches;
- * larger T runs the dispatch + grouped-GEMM path (or the GEMV path for
- * formats it lacks). */
+ * can make a wait give up.  Other T <= 4 cases run in four to six launches
+ * (T <= 8 when no grouped-GEMM kernel serves the formats); larger T runs the
+ * dispatch + grouped-GEMM path (or the GEMV path for formats it lacks). */
 moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
                        const uint16_t* w_router, const float* bias,
                        const moe_ffn_weights* routed /*host struct*/,
@@ -216,12 +244,24 @@ moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_
                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* The whole layer from the pre-norm rows h: stage M (norm, required), then
+ * exactly moe_forward on the normalised x.  x_out (bf16 [T][H], NULL ok)
+ * receives x.  The batched path normalises inside its fused router launch,
+ * the single launch stages the normalised rows in LDS itself; the other
+ * small-T paths run the norm as a first launch. */
+moe_status moe_forward_norm(const moe_config* cfg /*host*/, const uint16_t* h, int32_t T,
+                            const moe_norm* norm /*host struct*/, const uint16_t* w_router, const float* bias,
+                            const moe_ffn_weights* routed /*host struct*/,
+                            const moe_ffn_weights* shared /*host struct or NULL*/, uint16_t* out,
+                            int32_t* topk_ids_out, float* topk_w_out, uint16_t* x_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* moe_forward without a workspace argument, for callers that cannot
  * allocate (code under graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, paths and results as moe_forward; the
  * workspace is a 32 MiB device array inside the library, one per GPU,
- * resolved on the first call on a device (whose counter block that call
- * clears on `stream`) and held until the process ends.  No call allocates
+ * resolved on the first call on a device (whose 48 KiB counter block that
+ * call clears on `stream`) and held until the process ends.  No call allocates
  * memory or creates a stream.  Every call on a GPU uses that GPU's one
  * array: calls that overlap on one GPU (several streams or threads) race,
  * so order them on one stream.  The shared expert always runs in order on

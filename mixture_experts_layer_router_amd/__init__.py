@@ -37,6 +37,10 @@ class Config(ctypes.Structure):
     ]
 
 
+class Norm(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 class FfnWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("gate", "up", "down", "gate_s", "up_s", "down_s")]
 
@@ -63,6 +67,10 @@ def _lib():
             "moe_forward": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
             "moe_workspace_check": (_i32, [_vp, _sz, _i32, _vp]),
+            "moe_route_dispatch": (_i32, [P(Config), _vp, _i32, P(Norm), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _sz, _vp]),
+            "moe_forward_norm": (_i32, [P(Config), _vp, _i32, P(Norm), _vp, _vp, P(FfnWeights), P(FfnWeights), _vp,
+                                        _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_forward_noalloc": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp,
                                            _vp, _vp]),
             "moe_debug_ws_offset": (_i32, [P(Config), _i32, _i32, P(_sz)]),
@@ -81,7 +89,7 @@ def _lib():
 
 
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_workspace_check", "moe_debug_ws_offset",
+           "moe_combine", "moe_forward", "moe_forward_norm", "moe_route_dispatch", "moe_forward_noalloc", "moe_workspace_check", "moe_debug_ws_offset",
            "moe_debug_ffn_tile_rows", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
            "moe_debug_trace_count", "moe_debug_trace_name")
 
@@ -183,6 +191,28 @@ def ffn_tile_rows(cfg, which):
     return _lib().moe_debug_ffn_tile_rows(ctypes.byref(cfg), int(which))
 
 
+def make_norm(gamma, eps):
+    n = Norm(gamma.data_ptr(), float(eps))
+    n._keep = gamma
+    return n
+
+
+def route_dispatch(cfg, h, norm, w_router, bias, ids, w, offsets, perm_src, inv_pos, x_out, xq, xq_scale, ws,
+                   stream=None):
+    """norm: Norm or None."""
+    _check(_lib().moe_route_dispatch(ctypes.byref(cfg), _ptr(h), h.shape[0], None if norm is None else ctypes.byref(norm),
+                                     _ptr(w_router), _ptr(bias), _ptr(ids), _ptr(w), _ptr(offsets), _ptr(perm_src),
+                                     _ptr(inv_pos), _ptr(x_out), _ptr(xq), _ptr(xq_scale), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "moe_route_dispatch")
+
+
+def forward_norm(cfg, h, norm, w_router, bias, routed, shared, out, ids, w, x_out, ws, stream=None):
+    _check(_lib().moe_forward_norm(ctypes.byref(cfg), _ptr(h), h.shape[0], ctypes.byref(norm), _ptr(w_router),
+                                   _ptr(bias), ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
+                                   _ptr(out), _ptr(ids), _ptr(w), _ptr(x_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_forward_norm")
+
+
 def forward_noalloc(cfg, x, w_router, bias, routed, shared, out, ids, w, stream=None):
     """moe_forward on the library's own per-GPU device array (no workspace)."""
     _check(_lib().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), x.shape[0], _ptr(w_router), _ptr(bias),
@@ -249,5 +279,12 @@ class Layer:
         out = torch.empty(T, self.lc.hidden, dtype=torch.bfloat16, device=dev) if out is None else out
         ids = torch.empty(T, self.lc.topk, dtype=torch.int32, device=dev) if ids is None else ids
         w = torch.empty(T, self.lc.topk, dtype=torch.float32, device=dev) if w is None else w
-        forward(self.cfg, x, self.inp.w_router, self.inp.bias, self.routed, self.shared, out, ids, w, self.ws, stream)
+        if getattr(self.lc, "norm", False):
+            if not hasattr(self, "_norm"):
+                self._norm = make_norm(self.inp.gamma, self.lc.norm_eps)
+            forward_norm(self.cfg, x, self._norm, self.inp.w_router, self.inp.bias, self.routed, self.shared, out, ids,
+                         w, None, self.ws, stream)
+        else:
+            forward(self.cfg, x, self.inp.w_router, self.inp.bias, self.routed, self.shared, out, ids, w, self.ws,
+                    stream)
         return out, ids, w

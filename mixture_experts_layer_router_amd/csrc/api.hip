@@ -96,6 +96,7 @@ size_t wscale_stride(int wfmt, int N, int K) {  // scale elements per expert
 struct Ws {
   size_t counter, logits, ids, w, offsets, perm, inv, hist, tiles, ntiles;
   size_t xq, xqs, xs2, xs2s;  // routed-format x, shared-format x
+  size_t xn, rhist;           // normalised x (bf16), per-block expert counts of the fused router
   size_t h, hs, hsh, hshs;    // routed h (+scales), shared h (+scales)
   size_t yperm, ysh;
   size_t total;
@@ -136,6 +137,8 @@ Ws plan(const moe_config* c, int Tm) {
     s.ysh = take(T * H * 4);
   }
   s.yperm = take(TK * H * 2);
+  s.xn = take(T * H * 2);
+  s.rhist = take(((T + kRouteBlock - 1) / kRouteBlock) * E * 4);
   s.total = o;
   return s;
 }
@@ -232,6 +235,14 @@ hipError_t traced(const char* name, hipStream_t s, F&& f) {
 }
 #define LAUNCH(name, expr) HIP_TRY(traced(name, s_, [&] { return (expr); }))
 
+// stage M: the norm weight (null: no norm), its eps, and where the caller
+// wants the normalised x (null: nowhere)
+struct NormArgs {
+  const uint16_t* gamma = nullptr;
+  float eps = 0.f;
+  uint16_t* x_out = nullptr;
+};
+
 moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_t* wr, const float* bias, int* ids,
                     float* w, void* ws, const Ws& L, hipStream_t s) {
   const RouteParams rp = route_params(c);
@@ -241,23 +252,46 @@ moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_
     LAUNCH("topk", launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s));
     return MOE_OK;
   }
-  GemmParams g{};
-  g.A = x;
-  g.lda = c->hidden;
-  g.B0 = wr;
-  g.N = c->n_experts;
-  g.K = c->hidden;
-  g.M = T;
-  g.C = at<float>(ws, L.logits);
-  g.ldc = c->n_experts;
-  // N = E is at most one tile wide: split K so the launch fills the chip; the
-  // top-k adds the slices in a fixed order
-  // (N = E is small: the launcher keeps this on the 128-row kernel, 128-byte K steps)
-  const int mt = (T + kGemmBM - 1) / kGemmBM, steps = c->hidden * 2 / 128;
-  g.ksplit = std::max(1, std::min({kRouterMaxSplit, 256 / mt, steps}));
-  g.c_split = long(T) * c->n_experts;
-  LAUNCH("gemm_router_logits", launch_gemm(W_BF16, EPI_F32, g, s));
-  LAUNCH("topk", launch_topk(at<float>(ws, L.logits), T, bias, rp, ids, w, s, g.ksplit, g.c_split));
+  RouteFusedParams rf{};
+  rf.h = x;
+  rf.T = T;
+  rf.H = c->hidden;
+  rf.wr = wr;
+  rf.bias = bias;
+  rf.rp = rp;
+  rf.ids = ids;
+  rf.w = w;
+  LAUNCH("route_fused", launch_route_fused(rf, s));
+  return MOE_OK;
+}
+
+// The batched routing stack: stage M (if any), router, top-k, the routed
+// input in its activation format and the per-block counts in one launch
+// (route_fused.hip), then the stable scatter (offsets, perm_src, inv_pos and,
+// with `tiles`, the grouped-GEMM tile list of bm-row tiles).
+moe_status route_dispatch(const moe_config* c, const uint16_t* h, int T, const NormArgs& nm, const uint16_t* wr,
+                          const float* bias, int* ids, float* w, int* off, int* perm, int* inv, uint16_t* x_out,
+                          void* xq, void* xqs, int* tiles, int* ntiles, int bm, void* ws, const Ws& L, hipStream_t s) {
+  hipStream_t s_ = s;
+  RouteFusedParams rf{};
+  rf.h = h;
+  rf.gamma = nm.gamma;
+  rf.eps = nm.eps;
+  rf.T = T;
+  rf.H = c->hidden;
+  rf.wr = wr;
+  rf.bias = bias;
+  rf.rp = route_params(c);
+  rf.ids = ids;
+  rf.w = w;
+  rf.x_out = x_out;
+  rf.afmt = c->routed_afmt;
+  rf.xq = c->routed_afmt != A_NONE ? xq : nullptr;
+  rf.xqs = xqs;
+  rf.hist = at<int>(ws, L.rhist);
+  LAUNCH("route_fused", launch_route_fused(rf, s));
+  LAUNCH("permute", launch_permute_scatter(ids, T * c->topk, c->n_experts, rf.hist, kRouteBlock * c->topk, off, perm,
+                                           inv, tiles, ntiles, bm, s));
   return MOE_OK;
 }
 
@@ -343,10 +377,11 @@ moe_status shared_ffn(const moe_config* cfg, const uint16_t* x, int T, const moe
 // moe_forward on a given workspace.  side_ok: a shared expert too small to
 // fill the chip may run on the side stream (created on first use); false
 // keeps every launch on the caller's stream.
+// nm: stage M before the router (nm.gamma null: x is the layer input as given).
 moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
                         const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared, uint16_t* out,
                         int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                        bool side_ok) {
+                        bool side_ok, const NormArgs& nm = NormArgs{}) {
   hipStream_t s_ = stream;
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
@@ -359,10 +394,14 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
   if (has_shared && (st = check_weights(shared, cfg->shared_wfmt)) != MOE_OK) return st;
   for (const void* p : {(const void*)x, (const void*)w_router, (const void*)out, (const void*)ws})
     if (!aligned16(p)) return MOE_EALIGN;
+  if (nm.gamma && (!aligned16(nm.gamma) || (nm.x_out && !aligned16(nm.x_out)) || !(nm.eps >= 0.f)))
+    return nm.eps >= 0.f ? MOE_EALIGN : MOE_EINVAL;
   const Ws L = plan(cfg, T);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
 
   const int H = cfg->hidden, K = cfg->topk, E = cfg->n_experts, TK = T * K;
+  const bool norm = nm.gamma != nullptr;
+  uint16_t* xn = norm ? (nm.x_out ? nm.x_out : at<uint16_t>(ws, L.xn)) : nullptr;  // normalised x
   const int raf = cfg->routed_afmt, saf = cfg->shared_afmt;
   int* ids = topk_ids_out ? topk_ids_out : at<int>(ws, L.ids);
   float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
@@ -371,8 +410,19 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
   if (fp == 2 && !pairs_ok) return MOE_EUNSUPPORTED;
   const bool gemv = fp == 1 || fp == 3 || (fp != 2 && T <= kGemvMaxT) || !pairs_ok;
 
-  if (gemv && T <= kRouteGemvMaxT && fp != 3 && raf == A_NONE && size_t(T) * H * 2 <= size_t(kFusedXLdsMax) &&
-      H % 8 == 0 && (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt))) {
+  // T <= 8 with bf16 activations and one weight format: the single launch
+  // (unless a test forces the GEMM or the staged launches)
+  const bool single = fp != 2 && fp != 3 && T <= kRouteGemvMaxT && raf == A_NONE && H % 8 == 0 &&
+                      (!has_shared || (saf == A_NONE && cfg->shared_wfmt == cfg->routed_wfmt));
+  if (single) {
+    // x staged in LDS (with the norm applied there) up to kFusedXLdsMax bytes;
+    // above, the launch reads x from L2, normalised first by its own launch
+    NormArgs snm = nm;
+    if (norm && size_t(T) * H * 2 > size_t(kFusedXLdsMax)) {
+      LAUNCH("rmsnorm", launch_rmsnorm_rows(x, nm.gamma, nm.eps, T, H, xn, stream));
+      x = xn;
+      snm = NormArgs{};
+    }
     // small T, bf16 activations: the whole layer in one persistent launch
     FusedDecodeParams fp_{};
     DecodeParams& dp = fp_.d;
@@ -400,8 +450,16 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
     fp_.h = at<float>(ws, L.h);
     fp_.out = out;
     fp_.ctr = at<unsigned>(ws, L.counter);
+    dp.gamma = snm.gamma;
+    dp.eps = snm.eps;
+    dp.x_out = snm.x_out;
     LAUNCH("decode_fused", launch_fused_decode(fp_, stream));
     return MOE_OK;
+  }
+
+  if (norm && gemv) {  // the launches below read x: normalise it first
+    LAUNCH("rmsnorm", launch_rmsnorm_rows(x, nm.gamma, nm.eps, T, H, xn, stream));
+    x = xn;
   }
 
   if (gemv && T <= kRouteGemvMaxT) {
@@ -492,8 +550,11 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
   SideStream* side = nullptr;
   SideJoin joiner;  // declared after the lock: it joins before the lock is released
   float* ysh = nullptr;
-  if (!gemv && has_shared && side_ok &&
-      long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128) {
+  // the shared FFN forks onto the side stream as soon as its input exists:
+  // at once without a norm, after the fused router (which writes xn) with one
+  const bool fork = !gemv && has_shared && side_ok &&
+                    long((T + kGemmBM - 1) / kGemmBM) * ((cfg->shared_inter + 127) / 128) < 128;
+  auto fork_shared = [&](const uint16_t* xs_in) -> moe_status {
     side_lock.lock();
     side = side_stream(stream);
     if (side) {
@@ -501,11 +562,15 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
       HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
       joiner.side = side;
       joiner.caller = stream;
-      if ((st = shared_ffn(cfg, x, T, shared, ws, L, &ysh, side->s)) != MOE_OK) return st;
+      return shared_ffn(cfg, xs_in, T, shared, ws, L, &ysh, side->s);
     }
-  }
+    return MOE_OK;
+  };
+  if (fork && !norm && (st = fork_shared(x)) != MOE_OK) return st;
 
-  if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
+  if (gemv) {
+    if ((st = do_route(cfg, x, T, w_router, bias, ids, w, ws, L, stream)) != MOE_OK) return st;
+  }
 
   if (gemv) {  // T > kRouteGemvMaxT on the GEMV path: routed + shared gate/up in one launch
     const void* xr = x;
@@ -572,19 +637,22 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
     return MOE_OK;
   }
 
-  // batched path
+  // batched path: routing stack (fused router + scatter), routed GEMMs,
+  // shared GEMMs (side stream or in order), combine
   int* off = at<int>(ws, L.offsets);
   int* perm = at<int>(ws, L.perm);
   int* inv = at<int>(ws, L.inv);
   int* tiles = at<int>(ws, L.tiles);
   int* ntiles = at<int>(ws, L.ntiles);
   const int rbm = ffn_tile_rows(cfg->routed_wfmt, H, cfg->inter);
-  LAUNCH("permute", launch_permute(ids, TK, E, at<int>(ws, L.hist), off, perm, inv, tiles, ntiles, rbm, stream));
-  const void* xa = x;
+  if ((st = route_dispatch(cfg, x, T, nm, w_router, bias, ids, w, off, perm, inv, xn, at<void>(ws, L.xq),
+                           at<void>(ws, L.xqs), tiles, ntiles, rbm, ws, L, stream)) != MOE_OK)
+    return st;
+  const uint16_t* xin = norm ? xn : x;  // the layer input x
+  if (fork && norm && (st = fork_shared(xin)) != MOE_OK) return st;
+  const void* xa = xin;
   const void* xas = nullptr;
   if (raf != A_NONE) {
-    LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, raf, at<void>(ws, L.xq), at<void>(ws, L.xqs), nullptr,
-                              stream));
     xa = at<void>(ws, L.xq);
     xas = at<void>(ws, L.xqs);
   }
@@ -592,14 +660,14 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
                      at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
     return st;
   if (has_shared && !side) {  // in order on the caller's stream
-    const void* xs = x;
+    const void* xs = xin;
     const void* xss = nullptr;
     if (saf != A_NONE) {
       if (saf == raf) {
         xs = xa;
         xss = xas;
       } else {
-        LAUNCH("quant_rows", launch_quant_rows(x, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
+        LAUNCH("quant_rows", launch_quant_rows(xin, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
                                   nullptr, stream));
         xs = at<void>(ws, L.xs2);
         xss = at<void>(ws, L.xs2s);
@@ -843,6 +911,45 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* x, int32_t T, cons
                        int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   return forward_impl(cfg, x, T, w_router, bias, routed, shared, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream,
                       true);
+}
+
+moe_status moe_forward_norm(const moe_config* cfg, const uint16_t* h, int32_t T, const moe_norm* norm,
+                            const uint16_t* w_router, const float* bias, const moe_ffn_weights* routed,
+                            const moe_ffn_weights* shared, uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
+                            uint16_t* x_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!norm || !norm->gamma) return MOE_EINVAL;
+  NormArgs nm;
+  nm.gamma = norm->gamma;
+  nm.eps = norm->eps;
+  nm.x_out = x_out;
+  return forward_impl(cfg, h, T, w_router, bias, routed, shared, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream,
+                      true, nm);
+}
+
+moe_status moe_route_dispatch(const moe_config* cfg, const uint16_t* h, int32_t T, const moe_norm* norm,
+                              const uint16_t* w_router, const float* bias, int32_t* topk_ids, float* topk_w,
+                              int32_t* expert_offsets, int32_t* perm_src, int32_t* inv_pos, uint16_t* x_out, void* xq,
+                              void* xq_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!h || !w_router || !topk_ids || !topk_w || !expert_offsets || !perm_src || !inv_pos || !ws) return MOE_EINVAL;
+  if (norm && !norm->gamma) return MOE_EINVAL;
+  if (norm && !(norm->eps >= 0.f)) return MOE_EINVAL;
+  if (xq && (cfg->routed_afmt == A_NONE || !xq_scale)) return MOE_EINVAL;
+  for (const void* p : {(const void*)h, (const void*)w_router, (const void*)ws})
+    if (!aligned16(p)) return MOE_EALIGN;
+  if ((norm && !aligned16(norm->gamma)) || (x_out && !aligned16(x_out)) || (xq && !aligned16(xq))) return MOE_EALIGN;
+  const Ws L = plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  NormArgs nm;
+  if (norm) {
+    nm.gamma = norm->gamma;
+    nm.eps = norm->eps;
+  }
+  return route_dispatch(cfg, h, T, nm, w_router, bias, topk_ids, topk_w, expert_offsets, perm_src, inv_pos, x_out, xq,
+                        xq_scale, nullptr, nullptr, 0, ws, L, stream);
 }
 
 moe_status moe_forward_noalloc(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,

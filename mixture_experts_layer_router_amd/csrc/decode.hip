@@ -1,4 +1,4 @@
-// Single-launch small-batch MoE layer (T <= 4, bf16 activations, one weight
+// Single-launch small-batch MoE layer (T <= 8, bf16 activations, one weight
 // format for routed and shared experts): stages N, O, P1/Q1, P2/Q2 and the
 // sum of R of the DSV2-236B-MegaKernel README flowchart in one persistent
 // launch, so HBM keeps streaming weights across what would otherwise be four
@@ -259,8 +259,12 @@ MOE_DEV const MOE_GLOBAL uint8_t* uni(const void* p) {
 // is stored with agent-scope atomic stores (read by other workgroups inside
 // the launch once the phase is published).  pre() runs once every load has
 // been consumed and before the store.
-template <int WF, int NR, int NC, class Pre>
-MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u, const void* gs, const void* us,
+// 16 bytes of x as bf16 pairs, from LDS or (x in global memory) with a global load
+MOE_DEV u32x4 ldx4(const uint32_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+MOE_DEV u32x4 ldx4(const MOE_GLOBAL uint32_t* p) { return *reinterpret_cast<const MOE_GLOBAL u32x4*>(p); }
+
+template <int WF, int NR, int NC, class XP, class Pre>
+MOE_DEV void gate_up_lds(XP xl, int H, const void* g, const void* u, const void* gs, const void* us,
                          int i0, float* hrow, Pre pre) {
   constexpr int CW = Fmt<WF>::CW, EPL = Fmt<WF>::EPL, ES = Fmt<WF>::ES;
   constexpr int NS = WF == W_MXFP8 ? NR : 1;  // scales per chunk (FP8_B128: the rows share a 128-row block)
@@ -313,7 +317,7 @@ MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u
       uint32_t xp[EPL / 2];
 #pragma unroll
       for (int i = 0; i < EPL / 8; ++i) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xl + k / 2 + 4 * i);
+        const u32x4 v = ldx4(xl + k / 2 + 4 * i);
 #pragma unroll
         for (int q = 0; q < 4; ++q) xp[4 * i + q] = v[q];
       }
@@ -337,14 +341,17 @@ MOE_DEV void gate_up_lds(const uint32_t* xl, int H, const void* g, const void* u
   if (lane < NR) __hip_atomic_store(hrow + i0 + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int WF>
+// XG: x is read from global memory (L2) instead of being staged in LDS, for
+// T * H * 2 above kFusedXLdsMax: staging 80 KB per workgroup would leave one
+// workgroup per CU, too few loads in flight; x is then already normalised.
+template <int WF, bool XG, int MAXT>
 __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams p) {
-  // the T rows of x as bf16 pairs (T * H * 2 bytes of dynamic LDS)
+  // the T rows of x as bf16 pairs (T * H * 2 bytes of dynamic LDS; none with XG)
   extern __shared__ __attribute__((aligned(16))) uint32_t sx[];
-  __shared__ float part[4][kRouteGemvMaxT];
+  __shared__ float part[4][MAXT];
   __shared__ float dpart[4][kDR];
-  __shared__ int sids[kRouteGemvMaxT * 16];
-  __shared__ float sw[kRouteGemvMaxT * 16];
+  __shared__ int sids[MAXT * 16];
+  __shared__ float sw[MAXT * 16];
   __shared__ unsigned s_next;
   __shared__ int s_ok, s_last, s_rok;
   const DecodeParams& d = p.d;
@@ -361,8 +368,29 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   auto phase_of = [&](int i) { return i < b2 ? 0 : (i < b3 ? 1 : 2); };
   const unsigned epoch = __hip_atomic_load(c.epoch(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned tag = epoch % 0xffffffffu + 1u;  // in [1, 0xffffffff]: a zero-filled word is never ready
-  for (int i = tid; i < T * H / 8; i += 256)
-    reinterpret_cast<u32x4*>(sx)[i] = reinterpret_cast<const u32x4*>(d.x)[i];
+  const MOE_GLOBAL uint32_t* xg = reinterpret_cast<const MOE_GLOBAL uint32_t*>(uni(d.x));
+  auto xrow = [&](int t) {
+    if constexpr (XG) return xg + size_t(t) * H / 2;
+    else return static_cast<const uint32_t*>(sx) + size_t(t) * H / 2;
+  };
+  if constexpr (XG) {
+  } else if (d.gamma) {  // stage M: every workgroup normalises the T rows into LDS itself (wave t: row t's r)
+    __shared__ float srms[MAXT];
+    for (int t = wave; t < T; t += 4) {
+      const float r = row_rms_inv(d.x + size_t(t) * H, H, d.eps);
+      if (lane == 0) srms[t] = r;
+    }
+    __syncthreads();
+    for (int i = tid; i < T * H / 8; i += 256) {
+      const int t = (i * 8) / H;
+      const u32x4 xb = norm_chunk(d.x + size_t(t) * H, d.gamma, i * 8 - t * H, srms[t]);
+      reinterpret_cast<u32x4*>(sx)[i] = xb;
+      if (blockIdx.x == 0 && d.x_out) reinterpret_cast<u32x4*>(d.x_out)[i] = xb;
+    }
+  } else {
+    for (int i = tid; i < T * H / 8; i += 256)
+      reinterpret_cast<u32x4*>(sx)[i] = reinterpret_cast<const u32x4*>(d.x)[i];
+  }
   if (tid == 0) s_rok = 1;
   __syncthreads();
 
@@ -371,7 +399,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   // routed item waits for, starts at once)
   if (int(blockIdx.x) < E) {
     if (tid == 0) s_next = q + kQ * atomic_inc(c.head(q));
-    router_row(d.x, T, d.wr, d.rp, blockIdx.x, nullptr, part, false, sx, c.tagged(), tag);
+    router_row<MAXT>(d.x, T, d.wr, d.rp, blockIdx.x, nullptr, part, false, XG ? nullptr : sx, c.tagged(), tag);
   } else if (tid == 0) {
     s_next = q + kQ * atomic_inc(c.head(q));
   }
@@ -391,16 +419,16 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
     if (it < b2) {  // SU: 8 shared intermediate columns of one token
       const int i = it - b1, per = Is / kSUpCols;
       const int t = i / per, c0 = (i % per) * kSUpCols + wave * kSUR;
-      gate_up_lds<WF, kSUR, kUC>(sx + size_t(t) * H / 2, H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is,
+      gate_up_lds<WF, kSUR, kUC>(xrow(t), H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is,
                                  hand_over);
     } else {
-      if (!have_topk) {  // every workgroup routes all T tokens itself (wave t: token t)
-        if (wave < T) {
+      if (!have_topk) {  // every workgroup routes all T tokens itself (wave w: tokens w, w + 4)
+        for (int tt = wave; tt < T; tt += 4) {
           const TopkLayout L(d.rp, lane);
           float lg[kMpl];
-          if (!load_tagged_logits(d.rp, L, c.tagged() + size_t(wave) * E, d.bias, tag, lg, c.error()) && lane == 0)
+          if (!load_tagged_logits(d.rp, L, c.tagged() + size_t(tt) * E, d.bias, tag, lg, c.error()) && lane == 0)
             s_rok = 0;
-          topk_select(d.rp, L, lg, sids + wave * K, sw + wave * K);
+          topk_select(d.rp, L, lg, sids + tt * K, sw + tt * K);
         }
         __syncthreads();
         poisoned |= s_rok == 0;
@@ -420,7 +448,7 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
         const uint8_t* ue = static_cast<const uint8_t*>(p.u) + e * ws;
         const uint8_t* gse = p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr;
         const uint8_t* use = p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr;
-        gate_up_lds<WF, kUR, kUC>(sx + size_t(slot / K) * H / 2, H, ge, ue, gse, use, c0, p.h + size_t(slot) * I,
+        gate_up_lds<WF, kUR, kUC>(xrow(slot / K), H, ge, ue, gse, use, c0, p.h + size_t(slot) * I,
                                   hand_over);
       } else {  // DN: kDR output rows of one token over [shared Is | routed K*I]
         const int i = it - b3, nb = H / kDR;
@@ -511,31 +539,40 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   }
 }
 
-template <int WF>
+template <int WF, bool XG, int MAXT>
 hipError_t launch_fused(const FusedDecodeParams& p, hipStream_t s) {
-  const size_t lds = size_t(p.d.T) * p.d.H * 2;
-  if (lds > size_t(kFusedXLdsMax) || p.d.H % 8) return hipErrorInvalidValue;
+  const size_t lds = XG ? 0 : size_t(p.d.T) * p.d.H * 2;
+  if (lds > size_t(kFusedXLdsMax) || p.d.H % 8 || p.d.T > MAXT || (XG && p.d.gamma))
+    return hipErrorInvalidValue;
   // resident capacity of the device for this LDS size (more workgroups would only queue)
   static int grid_for_dev[64] = {};
   static size_t lds_for_dev[64] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int grid = dev < 64 && lds_for_dev[dev] == lds ? grid_for_dev[dev] : 0;
+  int grid = dev < 64 && lds_for_dev[dev] == lds + 1 ? grid_for_dev[dev] : 0;
   if (grid == 0) {
     int per_cu = 0, cus = 0;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<WF>, 256, lds)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<WF, XG, MAXT>, 256, lds)) !=
+        hipSuccess)
       return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     grid = std::max(std::max(per_cu, 1) * cus, kQ);
     if (dev < 64) {
       grid_for_dev[dev] = grid;
-      lds_for_dev[dev] = lds;
+      lds_for_dev[dev] = lds + 1;  // +1: a cached size of 0 is not "unset"
     }
   }
   grid = std::max(grid, p.d.rp.E);  // one workgroup per router row
-  hipLaunchKernelGGL((fused_decode_kernel<WF>), dim3(grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((fused_decode_kernel<WF, XG, MAXT>), dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
+}
+
+template <int WF>
+hipError_t launch_fused_x(const FusedDecodeParams& p, hipStream_t s) {
+  if (size_t(p.d.T) * p.d.H * 2 > size_t(kFusedXLdsMax)) return launch_fused<WF, true, kRouteGemvMaxT>(p, s);
+  if (p.d.T <= 4) return launch_fused<WF, false, 4>(p, s);
+  return launch_fused<WF, false, kRouteGemvMaxT>(p, s);
 }
 
 }  // namespace
@@ -543,9 +580,9 @@ hipError_t launch_fused(const FusedDecodeParams& p, hipStream_t s) {
 hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s) {
   if (p.d.Is && p.d.swfmt != p.wfmt) return hipErrorInvalidValue;
   switch (p.wfmt) {
-    case W_BF16: return launch_fused<W_BF16>(p, s);
-    case W_FP8_B128: return launch_fused<W_FP8_B128>(p, s);
-    default: return launch_fused<W_MXFP8>(p, s);
+    case W_BF16: return launch_fused_x<W_BF16>(p, s);
+    case W_FP8_B128: return launch_fused_x<W_FP8_B128>(p, s);
+    default: return launch_fused_x<W_MXFP8>(p, s);
   }
 }
 

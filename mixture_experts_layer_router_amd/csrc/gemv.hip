@@ -111,7 +111,7 @@ template <int SWF, bool XSF32>
 __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeParams p) {
   __shared__ float part[4][kRouteGemvMaxT];
   if (int(blockIdx.x) < p.rp.E) {
-    router_row(p.x, p.T, p.wr, p.rp, blockIdx.x, p.logits, part);
+    router_row<kRouteGemvMaxT>(p.x, p.T, p.wr, p.rp, blockIdx.x, p.logits, part);
     return;
   }
   const long wid = long(blockIdx.x - p.rp.E) * 4 + (threadIdx.x >> 6);
@@ -126,11 +126,12 @@ template <int SWF>
 __global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeParams p) {
   const int wave = threadIdx.x >> 6, lane = lane_id();
   if (blockIdx.x == 0) {
-    if (wave >= p.T) return;
     const TopkLayout L(p.rp, lane);
-    float lg[kMpl];
-    topk_load(p.rp, L, p.logits + size_t(wave) * p.rp.E, p.bias, lg);
-    topk_select(p.rp, L, lg, p.ids + wave * p.rp.K, p.w + wave * p.rp.K);
+    for (int t = wave; t < p.T; t += 4) {
+      float lg[kMpl];
+      topk_load(p.rp, L, p.logits + size_t(t) * p.rp.E, p.bias, lg);
+      topk_select(p.rp, L, lg, p.ids + t * p.rp.K, p.w + t * p.rp.K);
+    }
     return;
   }
   __shared__ float part[DW][RD];

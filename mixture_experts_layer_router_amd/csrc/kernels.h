@@ -15,7 +15,7 @@ struct RouteParams {
   float scale;
 };
 // Small-T router logits: one workgroup per expert row.  T <= kRouteGemvMaxT.
-constexpr int kRouteGemvMaxT = 4;
+constexpr int kRouteGemvMaxT = 8;
 hipError_t launch_route_logits(const uint16_t* x, int T, const uint16_t* wr, const RouteParams& p,
                                float* logits, hipStream_t s);
 // Top-k over precomputed fp32 logits [T][E] (bias added here).  The logits
@@ -25,6 +25,31 @@ hipError_t launch_topk(const float* logits, int T, const float* bias, const Rout
                        float* w, hipStream_t s, int nslice = 1, long slice_stride = 0);
 constexpr int kRouterMaxSplit = 16;  // K slices of the batched router GEMM
 
+// Batched routing in one launch (route_fused.hip): optional stage M RMSNorm,
+// router, top-k, the routed-format input and per-block expert counts, one
+// workgroup per kRouteBlock tokens.
+constexpr int kRouteBlock = 16;
+struct RouteFusedParams {
+  const uint16_t* h;      // bf16 [T][H]: the layer input x, or the pre-norm h when gamma is set
+  const uint16_t* gamma;  // bf16 [H] norm weight, or null (no norm)
+  float eps;
+  int T, H;
+  const uint16_t* wr;     // bf16 [E][H]
+  const float* bias;      // fp32 [E] or null
+  RouteParams rp;
+  int* ids;               // [T][K]
+  float* w;               // [T][K]
+  uint16_t* x_out;        // bf16 [T][H] normalised x (or a copy of x), or null
+  int afmt;               // format of xq / xqs
+  void* xq;               // codes u8 [T][H] in afmt (FP8_1X128 / MXFP8_1X32), or null
+  void* xqs;              // their scales
+  int* hist;              // int32 [ceil(T/kRouteBlock)][E] slot counts per block, or null
+};
+hipError_t launch_route_fused(const RouteFusedParams& p, hipStream_t s);
+// Stage M alone: x = bf16 RMSNorm(h) * gamma (the rounding of route_fused).
+hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* gamma, float eps, int T, int H, uint16_t* x,
+                               hipStream_t s);
+
 // ------------------------------------------------------------------ dispatch
 // ids [TK]; writes offsets [E+1], perm_src [TK], inv_pos [TK]; when tiles is
 // non-null also the grouped-GEMM tile list for row tiles of `bm` rows:
@@ -33,6 +58,10 @@ constexpr int kRouterMaxSplit = 16;  // K slices of the batched router GEMM
 constexpr size_t permute_hist_ints(int TK, int E) { return size_t((TK + 1023) / 1024) * size_t(E); }
 hipError_t launch_permute(const int* ids, int TK, int E, int* hist, int* offsets, int* perm_src, int* inv_pos,
                           int* tiles, int* ntiles, int bm, hipStream_t s);
+// The scatter alone, with counts given as hist rows of `fine` slots each
+// (fine <= 1024; row i counts slots [i*fine, (i+1)*fine)).
+hipError_t launch_permute_scatter(const int* ids, int TK, int E, const int* hist, int fine, int* offsets,
+                                  int* perm_src, int* inv_pos, int* tiles, int* ntiles, int bm, hipStream_t s);
 hipError_t launch_build_tiles(const int* offsets, int E, int rows, int bm, int* tiles, int* ntiles, hipStream_t s);
 inline int max_tiles(int rows, int E, int bm) { return (rows + bm - 1) / bm + E; }
 
@@ -158,7 +187,11 @@ hipError_t launch_gemv_down(const GemvDownParams& p, hipStream_t s);
 //   then routed gate/up (launch_gemv_gate_up) and routed down + combine
 //   (launch_gemv_down with ys_add = ysh).
 struct DecodeParams {
-  const uint16_t* x;  // bf16 [T][H] (router input)
+  const uint16_t* x;  // bf16 [T][H] (router input; the pre-norm h when gamma is set)
+  const uint16_t* gamma;  // single launch only: stage M norm weight bf16 [H], or null (must be null
+                          // when T * H * 2 > kFusedXLdsMax: x is then read already normalised)
+  float eps;
+  uint16_t* x_out;        // single launch only: the normalised x, bf16 [T][H], or null
   int T, H;
   const uint16_t* wr;
   const float* bias;
@@ -178,8 +211,8 @@ struct DecodeParams {
 hipError_t launch_decode_stage1(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_stage2(const DecodeParams& p, hipStream_t s);
 
-// Small-T layer with bf16 activations and one weight format for routed and
-// shared experts, in one persistent launch (decode.hip): router, top-k, shared
+// Small-T layer (T <= kRouteGemvMaxT) with bf16 activations and one weight
+// format for routed and shared experts, in one persistent launch (decode.hip): router, top-k, shared
 // and routed gate/up, down + combine, ordered by work queues and completion
 // counters in `ctr` (kFusedCtrBytes, zero before the first launch; every
 // launch leaves its queues and counters zero again; the sticky error word,
@@ -193,11 +226,11 @@ struct FusedDecodeParams {
   uint16_t* out;   // bf16 [T][H]
   unsigned* ctr;   // counter block
 };
-constexpr int kFusedCtrBytes = 32768;
+constexpr int kFusedCtrBytes = 49152;
 constexpr int kFusedErrorWord = 0;  // ctr[0] != 0: a bounded wait gave up (never expected)
 constexpr int kFusedEpochWord = 1;  // ctr[1]: launches so far modulo 0xffffffff, never reset
 constexpr int kFusedTagOff = 24576;  // bytes: tagged router logits, 64-bit [T][E]
-constexpr int kFusedXLdsMax = 65536;  // bytes of x (T * H bf16) the launch stages in LDS
+constexpr int kFusedXLdsMax = 65536;  // bytes of x (T * H bf16) the launch stages in LDS; above, x is read from L2
 hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ combine

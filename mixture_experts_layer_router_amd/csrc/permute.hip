@@ -129,23 +129,27 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int* __restri
   for (int i = tid; i < E; i += kChunk) hist[size_t(c) * E + i] = cnt[i];
 }
 
-// Stable scatter of one chunk.  Every workgroup reduces the chunk counts
-// itself (the expert totals, and the counts of the chunks before its own), so
-// no workgroup waits for another; workgroup 0 also writes the offsets and the
-// tile list.  With a single chunk (hist NULL) the counts come from the chunk.
+// Stable scatter of one chunk of per_wg slots.  The counts come in hist rows
+// of `fine` slots each (per_wg is a multiple of fine, at most 1024): every
+// workgroup reduces them itself (the expert totals, and the counts of the
+// rows before its own chunk), so no workgroup waits for another; workgroup 0
+// also writes the offsets and the tile list.  With a single chunk (hist NULL)
+// the counts come from the chunk.
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int* __restrict__ ids, int TK, int E,
-                                                               const int* __restrict__ hist, int nchunks,
-                                                               int* __restrict__ offsets, int* __restrict__ perm_src,
-                                                               int* __restrict__ inv_pos, int* tiles, int* ntiles,
-                                                               int bm) {
+                                                               const int* __restrict__ hist, int nchunks, int fine,
+                                                               int per_wg, int* __restrict__ offsets,
+                                                               int* __restrict__ perm_src, int* __restrict__ inv_pos,
+                                                               int* tiles, int* ntiles, int bm) {
   __shared__ int part[2][4][kMaxE];    // [before, total][quarter][expert]
   __shared__ int tot[kMaxE];           // slots of each expert
   __shared__ int first[kMaxE];         // position of this chunk's first slot of each expert
   __shared__ int wcnt[kMaxE][kWaves];  // per (expert, wave): count, then first position
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = blockIdx.x;
-  const int p = c * kChunk + tid;
-  const int e = p < TK ? ids[p] : -1;
+  const int p = c * per_wg + tid;
+  const bool mine = tid < per_wg && p < TK;
+  const int e = mine ? ids[p] : -1;
   const bool valid = e >= 0 && e < E;
+  const int rows_before = c * (per_wg / fine);  // hist rows wholly before this chunk
   for (int i = tid; i < kMaxE * kWaves; i += kChunk) (&wcnt[0][0])[i] = 0;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const uint64_t m = same_expert_lanes(e, valid);
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int* __rest
       for (int cc = q; cc < nchunks; cc += 4) {
         const int v = hist[size_t(cc) * E + x];
         total += v;
-        before += cc < c ? v : 0;
+        before += cc < rows_before ? v : 0;
       }
     }
     part[0][q][x] = before;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int* __rest
     const int pos = wcnt[e][wave] + rank;
     perm_src[pos] = p;
     inv_pos[p] = pos;
-  } else if (p < TK) {
+  } else if (mine) {
     inv_pos[p] = -1;
   }
   if (c == 0 && tiles) write_tiles(tot, E, bm, tiles, ntiles, &part[1][0][0]);
@@ -221,7 +225,19 @@ hipError_t launch_permute(const int* ids, int TK, int E, int* hist, int* offsets
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kChunk), 0, s, ids, TK, E,
-                     nchunks > 1 ? hist : nullptr, nchunks, offsets, perm_src, inv_pos, tiles, ntiles, bm);
+                     nchunks > 1 ? hist : nullptr, nchunks, kChunk, kChunk, offsets, perm_src, inv_pos, tiles, ntiles,
+                     bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scatter(const int* ids, int TK, int E, const int* hist, int fine, int* offsets,
+                                  int* perm_src, int* inv_pos, int* tiles, int* ntiles, int bm, hipStream_t s) {
+  if (TK <= 0) return hipSuccess;
+  if (fine <= 0 || fine > kChunk) return hipErrorInvalidValue;
+  const int per_wg = fine * (kChunk / fine);
+  const int nwg = (TK + per_wg - 1) / per_wg, nrows = (TK + fine - 1) / fine;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nwg), dim3(kChunk), 0, s, ids, TK, E, hist, nrows, fine, per_wg,
+                     offsets, perm_src, inv_pos, tiles, ntiles, bm);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ wr, RouteParams p,
                                                            float* __restrict__ logits) {
   __shared__ float part[4][kRouteGemvMaxT];
-  router_row(x, T, wr, p, blockIdx.x, logits, part);
+  router_row<kRouteGemvMaxT>(x, T, wr, p, blockIdx.x, logits, part);
 }
 
 // topk_load for logits summed over nslice split-K slices: every slice value

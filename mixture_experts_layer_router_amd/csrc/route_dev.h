@@ -89,11 +89,12 @@ MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[
   for (int j = 0; j < kMpl; ++j)
     if (lg[j] != kNegInfF) se += expf(lg[j] - m);  // NaN and +inf make s NaN
   const float s = wave_sum(se);
-  // selection keys: the logits, or all equal when the softmax is undefined
-  float key[kMpl];
+  // selection keys, in place of the logits: the logits, or all equal when
+  // the softmax is undefined (m and s above keep what the weights need)
   const bool degenerate = __any(bad);
 #pragma unroll
-  for (int j = 0; j < kMpl; ++j) key[j] = degenerate ? kNegInfF : lg[j];
+  for (int j = 0; j < kMpl; ++j) lg[j] = degenerate ? kNegInfF : lg[j];
+  float (&key)[kMpl] = lg;
   float kmx = kNegInfF;
 #pragma unroll
   for (int j = 0; j < kMpl; ++j) kmx = fmaxf(kmx, key[j]);
@@ -141,12 +142,14 @@ MOE_DEV void topk_select(const RouteParams& p, const TopkLayout& L, float (&lg)[
 // read there instead of from x.  tagged: when not null, the logits go there
 // instead, as 64-bit words (tag << 32 | float bits) stored with agent-scope
 // atomic stores, so a reader can tell this launch's value from an old one.
+// MAXT: the most tokens the caller passes (T <= MAXT <= kRouteGemvMaxT).
+template <int MAXT = kRouteGemvMaxT>
 MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* __restrict__ wr, const RouteParams& p,
-                        int e, float* __restrict__ logits, float (*part)[kRouteGemvMaxT], bool coherent = false,
+                        int e, float* __restrict__ logits, float (*part)[MAXT], bool coherent = false,
                         const uint32_t* xl = nullptr, uint64_t* tagged = nullptr, unsigned tag = 0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint16_t* row = wr + size_t(e) * p.H;
-  float acc[kRouteGemvMaxT] = {};
+  float acc[MAXT] = {};
   // 256 threads x 8 bf16 = 2048 columns per pass; 4 passes issued together
   if (xl) {
     for (int k0 = 0; k0 < p.H; k0 += 4 * 2048) {
@@ -158,7 +161,7 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
         const int k = min(k0 + c * 2048 + tid * 8, p.H - 8);
         const float on = k0 + c * 2048 + tid * 8 < p.H ? 1.0f : 0.0f;
 #pragma unroll
-        for (int t = 0; t < kRouteGemvMaxT; ++t) {
+        for (int t = 0; t < MAXT; ++t) {
           if (t >= T) break;  // uniform
           const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + (size_t(t) * p.H + k) / 2);
           float a = 0.f;
@@ -173,20 +176,22 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
     }
   } else
   for (int k0 = 0; k0 < p.H; k0 += 4 * 2048) {
-    u32x4 wv[4], xv[4][kRouteGemvMaxT];
+    u32x4 wv[4], xv[4][MAXT];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int k = min(k0 + c * 2048 + tid * 8, p.H - 8);
       wv[c] = *reinterpret_cast<const u32x4*>(row + k);
 #pragma unroll
-      for (int t = 0; t < kRouteGemvMaxT; ++t)
-        xv[c][t] = *reinterpret_cast<const u32x4*>(x + size_t(min(t, T - 1)) * p.H + k);
+      for (int t = 0; t < MAXT; ++t)
+        if (t < T || t < 4)  // rows 4 .. T-1 only when present (rows past T up to 4 reload row T-1, masked)
+          xv[c][t] = *reinterpret_cast<const u32x4*>(x + size_t(min(t, T - 1)) * p.H + k);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float on = k0 + c * 2048 + tid * 8 < p.H ? 1.0f : 0.0f;
 #pragma unroll
-      for (int t = 0; t < kRouteGemvMaxT; ++t) {
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= 4 && t >= T) break;  // uniform
         float a = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -198,7 +203,7 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
     }
   }
 #pragma unroll
-  for (int t = 0; t < kRouteGemvMaxT; ++t) {
+  for (int t = 0; t < MAXT; ++t) {
     const float v = wave_sum(acc[t]);
     if (lane == 0) part[wave][t] = v;
   }
@@ -213,6 +218,49 @@ MOE_DEV void router_row(const uint16_t* __restrict__ x, int T, const uint16_t* _
     else
       logits[tid * p.E + e] = v;
   }
+}
+
+// ------------------------------------------------------------------ stage M
+// RMSNorm of one bf16 row (DSV2-236B-MegaKernel flowchart, stage M):
+// r = fl32(1 / sqrt(mean(h^2) + eps)) with the mean in float64 (the squares
+// of bf16 values are exact, so only the additions round), and
+// x = bf16(fl32(fl32(h * gamma) * r)), each step rounded to nearest even.
+
+MOE_DEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// r of one row, computed by one whole wave (every lane gets it); H % 8 == 0
+MOE_DEV float row_rms_inv(const uint16_t* row, int H, float eps) {
+  double acc = 0.0;
+  for (int c = lane_id() * 8; c < H; c += 512) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xffff0000u);
+      acc = fma(lo, lo, acc);
+      acc = fma(hi, hi, acc);
+    }
+  }
+  acc = wave_sum_d(acc);
+  return float(1.0 / sqrt(acc / double(H) + double(eps)));
+}
+
+// x for 8 columns (4 bf16 pairs) of h with their gamma
+MOE_DEV u32x4 norm_pairs(u32x4 hv, u32x4 gv, float r) {
+  u32x4 xb;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = (__uint_as_float(hv[q] << 16) * __uint_as_float(gv[q] << 16)) * r;
+    const float hi = (__uint_as_float(hv[q] & 0xffff0000u) * __uint_as_float(gv[q] & 0xffff0000u)) * r;
+    xb[q] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  }
+  return xb;
+}
+MOE_DEV u32x4 norm_chunk(const uint16_t* row, const uint16_t* gamma, int c, float r) {
+  return norm_pairs(*reinterpret_cast<const u32x4*>(row + c), *reinterpret_cast<const u32x4*>(gamma + c), r);
 }
 
 // Load one token's logits (+ bias) into the layout.  The logits may be the sum

@@ -11,6 +11,7 @@ Sources (page title, section):
   max over 8 groups x 20, top-3 groups, top-6 experts, w = score x 16.0),
   P1/Q1 (gate+up, SiLU(g) x u), P2/Q2 (down), R (h += shared_out + routed);
   "Results" (per-128 block-scaled FP8).
+  Stage M (post-attention RMSNorm with weight gamma4) precedes the router.
 * Mixture-of-Kittens, Abstract and Figure 1 (GPU-side router projection,
   top-k and dispatch scheduling; token dispatch into expert FFNs, token
   combine); Table 2 caption (MXFP8 routed experts, BF16 shared expert).
@@ -25,6 +26,6 @@ routines, closed forms, brute force, invariants).
 """
 from .fp8 import e4m3_decode, e4m3_encode, e8m0_decode  # noqa: F401
 from .moe import (  # noqa: F401
-    bf16_to_f64, dequant_weight, quant_act, route, route_margins, permute,
+    bf16_to_f64, f32_to_bf16_bits, rmsnorm, dequant_weight, quant_act, route, route_margins, permute,
     expert_ffn, combine, forward, forward_tokens, forward_dense_masked, OracleResult,
 )

@@ -161,6 +161,37 @@ def quant_act(v, afmt, return_codes=False):
     raise ValueError(afmt)
 
 
+# ------------------------------------------------------------- stage M norm
+
+def rmsnorm(h, gamma, eps):
+    """Stage M of the DSV2-236B-MegaKernel flowchart (post-attention RMSNorm
+    with weight gamma), producing the layer's bf16 input x.
+
+    h, gamma: bf16 (uint16 bits or torch bf16) [T][H] and [H]; eps: float.
+    ms = mean(h^2) over the row (float64; the squares of bf16 values are
+    exact); r = fl32(1 / sqrt(ms + eps)); x = bf16(fl32(fl32(h * gamma) * r))
+    with round-to-nearest-even at each step.  The pages do not fix the
+    precision of the norm: the rounding points are those of a float32 norm
+    whose output is the bf16 activation the router and the experts read.
+    Returns x as uint16 bf16 bits [T][H] and r float32 [T].
+    """
+    hf = bf16_to_f64(h)
+    g32 = bf16_to_f64(gamma).astype(np.float32)
+    ms = np.sum(hf * hf, axis=1) / hf.shape[1]
+    r = (1.0 / np.sqrt(ms + np.float64(np.float32(eps)))).astype(np.float32)
+    p = hf.astype(np.float32) * g32[None, :]                    # exact: 8 x 8 significant bits
+    xn = (p * r[:, None]).astype(np.float32)                    # one fp32 rounding
+    return f32_to_bf16_bits(xn), r
+
+
+def f32_to_bf16_bits(v):
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return np.where(nan, 0x7FC0, rounded).astype(np.uint16)
+
+
 # ------------------------------------------------------------------ routing
 
 def _group_view(cfg):
@@ -336,11 +367,15 @@ class OracleResult:
     out: np.ndarray
 
 
-def forward(cfg, x, w_router, bias, routed, shared):
+def forward(cfg, x, w_router, bias, routed, shared, norm=None):
     """Whole layer.  x, w_router: bf16 (uint16 bits or torch bf16); bias f32 or
     None; routed/shared: objects with .fmt and .expert(e) -> (gate, up, down,
     gate_s, up_s, down_s) host arrays.  Output out is the unrounded float64
-    sum_j w_j * Y_j + S (stage R without the residual)."""
+    sum_j w_j * Y_j + S (stage R without the residual).
+    norm: None, or (gamma, eps): x is then the pre-norm h and the layer runs
+    on rmsnorm(h, gamma, eps) (stage M before stage N)."""
+    if norm is not None:
+        x, _ = rmsnorm(x, norm[0], norm[1])
     xf = bf16_to_f64(x)
     wr = bf16_to_f64(w_router)
     b = None if bias is None else _f64(bias)

@@ -8,5 +8,5 @@ here because the layer consumes already-quantised weights, the way the
 DSV2-236B-MegaKernel README ("Layout": the block-FP8 quantiser) quantises a
 checkpoint offline before any forward pass.
 """
-from .configs import CONFIGS, LayerConfig, get_config  # noqa: F401
+from .configs import CONFIGS, LayerConfig, get_config, with_norm  # noqa: F401
 from .generate import LayerInputs, ExpertWeights, make_inputs, make_experts, redraw_tokens, draw_tokens  # noqa: F401

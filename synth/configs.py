@@ -43,6 +43,8 @@ class LayerConfig:
     zipf_bias: float = 0.0  # >0: router bias b[e] = -s*ln(rank_e)
     x_sigma: float = 1.0
     w_sigma: float = 0.02
+    norm: bool = False      # stage M RMSNorm first: x is then the pre-norm h
+    norm_eps: float = 1e-6
 
     def with_tokens(self, t):
         return replace(self, tokens=t)
@@ -63,6 +65,13 @@ CONFIGS = [
     LayerConfig("dsv2_4096tok_zipf", 4, 4096, 5120, 160, 8, 3, 6, 16.0, 1536, 3072,
                 "fp8_b128", "fp8_b128", "fp8_1x128", "fp8_1x128", zipf_bias=1.2),
 ]
+
+
+def with_norm(cfg, h_sigma=3.0):
+    """The same layer preceded by the stage M RMSNorm (DSV2-236B-MegaKernel
+    flowchart, stage M: post-attention RMSNorm before the router GEMV): the
+    input is the pre-norm h ~ N(0, h_sigma^2), gamma ~ 1 + N(0, 0.1^2)."""
+    return replace(cfg, name=cfg.name + "_norm", norm=True, x_sigma=h_sigma)
 
 
 def get_config(name_or_index):

@@ -7,8 +7,9 @@ DeepSeek-V4.1 Flash Kernel Journey", section "Benchmarking Honestly".  The
 same seed gives the same values on one device type; a test draws once and
 hands the very same tensors to both the HIP path and the oracle.
 
-kind: 0 tokens x, 1 router weight, 2 router-bias ranks, 3/4/5 routed
-gate/up/down, 6/7/8 shared gate/up/down, 9 per-token redraws.
+kind: 0 tokens x (the pre-norm h for a layer with the stage M norm), 1
+router weight, 2 router-bias ranks, 3/4/5 routed gate/up/down, 6/7/8 shared
+gate/up/down, 9 per-token redraws, 10 the norm weight gamma.
 
 Values are fp32 N(0,1)*sigma, then rounded to bf16 (torch RNE) or quantised
 to e4m3fn codes with per-format scales.  The weight quantisers below only
@@ -141,6 +142,7 @@ class LayerInputs:
     routed: ExpertWeights
     shared: Optional[ExpertWeights]
     replica: int = 0
+    gamma: Optional[torch.Tensor] = None   # bf16 [H] norm weight (norm layers)
 
     @property
     def device(self):
@@ -162,12 +164,15 @@ def make_inputs(cfg: LayerConfig, device="cpu", replica=0, with_experts=True) ->
         g.manual_seed(seed_of(cfg.index, replica, 2, 0))
         ranks = torch.randperm(cfg.n_experts, generator=g).to(torch.float32) + 1.0
         bias = (-cfg.zipf_bias * torch.log(ranks)).to(device)
+    gamma = None
+    if cfg.norm:
+        gamma = (1.0 + 0.1 * _randn((cfg.hidden,), seed_of(cfg.index, replica, 10, 0), device)).to(torch.bfloat16)
     routed = shared = None
     if with_experts:
         routed = make_experts(cfg, False, device, replica)
         if cfg.shared_inter > 0:
             shared = make_experts(cfg, True, device, replica)
-    return LayerInputs(cfg, x.contiguous(), wr.contiguous(), bias, routed, shared, replica)
+    return LayerInputs(cfg, x.contiguous(), wr.contiguous(), bias, routed, shared, replica, gamma)
 
 
 def redraw_tokens(inp: LayerInputs, tokens, attempt: int):

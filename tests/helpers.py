@@ -16,7 +16,10 @@ def ensure_margin(inp, max_attempts=100):
     bias = None if inp.bias is None else inp.bias.detach().cpu().double().numpy()
     todo = np.arange(cfg.tokens)
     for attempt in range(max_attempts):
-        x = oracle.bf16_to_f64(inp.x[torch.as_tensor(todo, device=inp.x.device)])
+        rows = inp.x[torch.as_tensor(todo, device=inp.x.device)]
+        if cfg.norm:   # the router reads the normalised x
+            rows, _ = oracle.rmsnorm(rows, inp.gamma, cfg.norm_eps)
+        x = oracle.bf16_to_f64(rows)
         logits = x @ wr.T
         if bias is not None:
             logits = logits + bias
@@ -27,6 +30,11 @@ def ensure_margin(inp, max_attempts=100):
         synth.redraw_tokens(inp, bad, attempt)
         todo = bad
     raise RuntimeError("could not meet the routing margin")
+
+
+def norm_of(inp):
+    """The oracle's norm argument for a layer's inputs (None without a norm)."""
+    return (inp.gamma, inp.cfg.norm_eps) if inp.cfg.norm else None
 
 
 def rel_err(got, ref):

@@ -259,8 +259,8 @@ def test_forward_small(name, path, monkeypatch):
     cfg = SMALL[name]
     if path == "gemm" and not pairs_ok(cfg):
         pytest.skip("no GEMM kernel for this format pair")
-    if path == "staged" and cfg.tokens > 4:
-        pytest.skip("the staged small-T path serves T <= 4")
+    if path == "staged" and cfg.tokens > 8:
+        pytest.skip("the staged small-T path serves T <= 8")
     if path != "auto":
         monkeypatch.setenv("MOE_FORCE_PATH", path)
     inp = gpu_inputs(cfg)
@@ -315,7 +315,7 @@ def test_forward_full_size(cfgname):
     assert np.array_equal(outs[0][1], r.ids)
     assert np.max(np.abs(outs[0][2] - r.w) / r.w) <= WTOL
     assert rel_err(oracle.bf16_to_f64(outs[0][0].view(np.uint16)), r.out) <= TOL
-    if cfg.tokens > 4:
+    if cfg.tokens > 8:   # the batched path (T <= 8 runs the single launch here)
         _check_dispatch(cfg, layer, r)
 
 
@@ -360,9 +360,8 @@ def test_shared_ffn_dense_large_tiles(rows):
     assert rel_err(y.cpu().numpy(), ref) <= TOL
 
 
-# The DeepSeek-V2 layer at verify-sized batches: T <= 4 runs the single
-# launch (x in LDS: 40 KB at T = 4), T = 5..8 the GEMV launches with FP8
-# block-scaled weights against bf16 x.
+# The DeepSeek-V2 layer at verify-sized batches, all in the single launch
+# (x in LDS: 80 KB at T = 8).
 @pytest.mark.parametrize("T", [2, 4, 5, 8])
 def test_forward_dsv2_small_m(T):
     cfg = synth.get_config(1).derive(tokens=T)
@@ -379,14 +378,18 @@ def test_forward_dsv2_small_m(T):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-@pytest.mark.parametrize("T", [5, 6, 7, 8])
-def test_forward_b128_bf16x_gemv_branch(T):
-    """FP8 block-scaled weights with bf16 activations above the single-launch
-    size: the GEMV launches (router GEMM, top-k, gate/up, down + combine)."""
+@pytest.mark.parametrize("T,path", [(5, "auto"), (8, "auto"), (5, "staged"), (7, "staged"), (8, "gemv"),
+                                    (12, "auto"), (21, "auto")])
+def test_forward_b128_bf16x_small_t(T, path, monkeypatch):
+    """FP8 block-scaled weights with bf16 activations: T <= 8 in the single
+    launch (auto) or the staged launches; above that the GEMV launches
+    (routed + shared gate/up in one launch, down + combine in another)."""
     cfg = small_cfg(1, tokens=T, hidden=640, n_experts=24, n_groups=4, topk_groups=2, topk=5, inter=384,
                     shared_inter=512)
+    if path != "auto":
+        monkeypatch.setenv("MOE_FORCE_PATH", path)
     inp = gpu_inputs(cfg)
-    say(f"[forward b128 bf16-x] T={T}")
+    say(f"[forward b128 bf16-x] T={T} {path}")
     out, ids, w = _forward(cfg, inp)
     r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
     assert np.array_equal(ids.cpu().numpy(), r.ids)
@@ -478,19 +481,19 @@ def _queue_words(layer):
 
 def test_single_launch_queue_across_calls():
     """The single-launch small-T path over many calls on one workspace, with
-    T changing between 1 and 4 and two layers interleaved on one stream:
+    T changing between 1 and 8 and two layers interleaved on one stream:
     every output matches the oracle and the queue state is zero after each
     call (no bounded wait gave up, every counter reset) but for the epoch
     word, which each call advances by one."""
     layers = []
     for name in ("dsv2_like_4tok", "bf16_1tok"):
-        cfg = SMALL[name].derive(tokens=4)
+        cfg = SMALL[name].derive(tokens=8)
         inp = gpu_inputs(cfg)
         r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
         layers.append((name, moe.Layer(cfg, inp), inp, r))
     for it in range(12):
         for name, layer, inp, r in layers:
-            T = 1 + (it * 3 + len(name)) % 4
+            T = 1 + (it * 3 + len(name)) % 8
             say(f"[single-launch] {name} call {it} T={T}")
             out, ids, w = layer.forward(inp.x[:T].contiguous())
             torch.cuda.synchronize()
