@@ -29,3 +29,4 @@ from .moe import (  # noqa: F401
     bf16_to_f64, f32_to_bf16_bits, rmsnorm, dequant_weight, quant_act, route, route_margins, permute,
     expert_ffn, combine, forward, forward_tokens, forward_dense_masked, OracleResult,
 )
+from .backward import backward, ffn_backward, BackwardResult  # noqa: F401

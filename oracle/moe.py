@@ -56,6 +56,14 @@ def bf16_to_f64(a):
     return u.view(np.float32).astype(np.float64)
 
 
+def as_f64(a):
+    """bf16 (uint16 bits or torch bf16) -> float64; float64 arrays pass through
+    (the finite-difference pins perturb float64 parameters)."""
+    if isinstance(a, np.ndarray) and a.dtype == np.float64:
+        return a
+    return bf16_to_f64(a)
+
+
 def dequant_weight(codes, scales, fmt):
     """Weight matrix [N][K] -> float64.
 
@@ -68,6 +76,8 @@ def dequant_weight(codes, scales, fmt):
     """
     if fmt == "bf16":
         return bf16_to_f64(codes)
+    if fmt == "f64":   # float64 weights as given (finite-difference pins)
+        return np.asarray(codes, dtype=np.float64)
     codes = np.asarray(codes, dtype=np.uint8)
     N, K = codes.shape
     out = np.empty((N, K))
@@ -376,8 +386,8 @@ def forward(cfg, x, w_router, bias, routed, shared, norm=None):
     on rmsnorm(h, gamma, eps) (stage M before stage N)."""
     if norm is not None:
         x, _ = rmsnorm(x, norm[0], norm[1])
-    xf = bf16_to_f64(x)
-    wr = bf16_to_f64(w_router)
+    xf = as_f64(x)
+    wr = as_f64(w_router)
     b = None if bias is None else _f64(bias)
     r = route(xf, wr, b, cfg)
     T, K = r["ids"].shape
