@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer µs @B=1 (HBM GB/s, %peak); TFLOP/s @2048 tok (%FP8 MFMA peak)"
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="skip the 2048-token workload")
     ap.add_argument("--no-small-m", action="store_true", help="skip the 2-8 token DeepSeek-V2 layers")
     ap.add_argument("--no-batched", action="store_true", help="skip the 256- and 4096-token DeepSeek-V2 layers")
+    ap.add_argument("--no-backward", action="store_true", help="skip the bf16 backward of the 2048-token layer")
+    ap.add_argument("--backward-only", action="store_true", help="only run the backward (for profiling its kernels)")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--secondary-only", action="store_true",
                     help="only run the 2048-token workload (for profiling its kernels)")
@@ -165,6 +168,9 @@ def main():
     if args.secondary_only:
         print(json.dumps({"secondary": secondary(args, moe, synth, torch)}), flush=True)
         return
+    if args.backward_only:
+        print(json.dumps({"backward": backward(moe, synth, torch)}), flush=True)
+        return
     if args.batched_only:
         print(json.dumps({"batched": batched(moe, synth, torch, names=(args.batched_only,))}), flush=True)
         return
@@ -250,6 +256,8 @@ def main():
         out["small_m"] = small_m(moe, synth, torch)
     if not args.no_batched:
         out["batched"] = batched(moe, synth, torch)
+    if not args.no_backward:
+        out["backward"] = backward(moe, synth, torch)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, reps[0], layers[0], torch)
@@ -406,6 +414,62 @@ def secondary(args, moe, synth, torch):
         "flops_per_layer": flops,
         "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in kern.items()},
     }
+
+
+def backward_config(synth):
+    """The 2,048-token H=7168 layer with bf16 weights and unquantised
+    activations: the shape the backward is measured on."""
+    return synth.get_config("h7168_2048tok_mx").derive(name="h7168_2048tok_bf16", routed_wfmt="bf16",
+                                                        shared_wfmt="bf16", routed_afmt="none", shared_afmt="none")
+
+
+def backward(moe, synth, torch, steps=5):
+    """The layer's backward (Mixture-of-Kittens, Table 1) on the 2,048-token
+    H=7168 layer in bf16: us per call, and the matrix rate of the flops it
+    executes (routed: the recomputed gate/up/down and six backward GEMM
+    passes, 9 x 2 TK H I; shared: the recomputed gate/up and six passes,
+    8 x 2 T H Is; router: logits, dWr and dl Wr, 3 x 2 T E H) against the
+    dense bf16 matrix peak."""
+    cfg = backward_config(synth)
+    inp = synth.make_inputs(cfg, "cuda:0")
+    T, H, K, I, Is, E = cfg.tokens, cfg.hidden, cfg.topk, cfg.inter, cfg.shared_inter, cfg.n_experts
+    c = moe.make_config(cfg)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(synth.generate.seed_of(cfg.index, 0, 11, T))
+    dy = torch.randn(T, H, generator=g, device="cuda:0").to(torch.bfloat16)
+    ws = torch.empty(moe.backward_workspace_size(c, T), dtype=torch.uint8, device="cuda:0")
+    bf = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda:0")
+    dx, dr, db = bf(T, H), bf(E, H), torch.empty(E, dtype=torch.float32, device="cuda:0")
+    rg = moe.make_grads(bf(E, I, H), bf(E, I, H), bf(E, H, I))
+    sg = moe.make_grads(bf(1, Is, H), bf(1, Is, H), bf(1, H, Is))
+    rw, sw = moe.weights_of(inp.routed), moe.weights_of(inp.shared)
+    call = lambda: moe.backward(c, inp.x, inp.w_router, inp.bias, rw, sw, dy, dx, dr, db, rg, sg, ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record()
+        call()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    us = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
+    with moe.LaunchTrace(256) as tr:
+        call()
+    kern = {}
+    for name, ms in tr.kernels():
+        kern[name] = round(kern.get(name, 0.0) + ms * 1e3, 2)
+    flops = 2.0 * T * K * H * I * 9 + 2.0 * T * H * Is * 8 + 2.0 * T * E * H * 3
+    med = statistics.median(us)
+    del inp, ws, dy, dx, dr, db, rg, sg
+    torch.cuda.empty_cache()
+    return {"workload": "h7168_2048tok_bf16: 2,048 tokens, H=7168, 32 experts flat top-4, I=2048, bf16 routed + "
+                        "bf16 shared 2048, unquantised activations",
+            "us_per_call": {"median": round(med, 1), "min": round(us[0], 1), "max": round(us[-1], 1),
+                            "calls": steps},
+            "flops_per_call": flops, "tflops": round(flops / (med * 1e-6) / 1e12, 1),
+            "frac_bf16_peak": round(flops / (med * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "kernels_us": kern}
 
 
 def cpu_baseline(cfg, inp, lay, torch):

@@ -256,6 +256,41 @@ moe_status moe_forward_norm(const moe_config* cfg /*host*/, const uint16_t* h, i
                             int32_t* topk_ids_out, float* topk_w_out, uint16_t* x_out, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* Gradient buffers of one set of experts (device pointers, bf16):
+ * gate, up [n][I][H]; down [n][H][I]; n = E for routed, 1 for shared. */
+typedef struct {
+  void* gate;
+  void* up;
+  void* down;
+} moe_ffn_grads;
+
+/* Bytes of workspace moe_backward needs for up to max_tokens tokens
+ * (MOE_EUNSUPPORTED for formats it does not serve). */
+moe_status moe_backward_workspace_size(const moe_config* cfg /*host*/, int32_t max_tokens,
+                                       size_t* bytes /*host*/);
+
+/* The layer's backward pass (Mixture-of-Kittens, Table 1: the MoE layer's
+ * backward beside its forward), for bf16 weights and unquantised
+ * activations (MOE_EUNSUPPORTED otherwise).  Given dy bf16 [T][H], the
+ * gradient of the layer output out = sum_j w_j Y_j + S of moe_forward on the
+ * same x and weights, it writes the gradients of <dy, out>:
+ *   dx bf16 [T][H]; d_router bf16 [E][H]; d_bias fp32 [E] (NULL to skip);
+ *   d_routed (every expert's gate, up, down; zero for experts no token
+ *   chose) and d_shared (NULL when there is no shared expert), bf16.
+ * The routing is recomputed (the same ids as the forward: the selection is
+ * piecewise constant, so gradients flow only through the routing weights
+ * w = route_scale * softmax(logits)[id]); so are the gate/up products and
+ * the routed outputs.  Every output is overwritten, none accumulated.
+ * Reductions run in a fixed order: repeated calls give identical bits. */
+moe_status moe_backward(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,
+                        const uint16_t* w_router, const float* bias,
+                        const moe_ffn_weights* routed /*host struct*/,
+                        const moe_ffn_weights* shared /*host struct or NULL*/, const uint16_t* dy,
+                        uint16_t* dx, uint16_t* d_router, float* d_bias,
+                        const moe_ffn_grads* d_routed /*host struct*/,
+                        const moe_ffn_grads* d_shared /*host struct or NULL*/, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
 /* moe_forward without a workspace argument, for callers that cannot
  * allocate (code under graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, paths and results as moe_forward; the

@@ -41,6 +41,10 @@ class Norm(ctypes.Structure):
     _fields_ = [("gamma", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
+class FfnGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("gate", "up", "down")]
+
+
 class FfnWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("gate", "up", "down", "gate_s", "up_s", "down_s")]
 
@@ -67,6 +71,9 @@ def _lib():
             "moe_forward": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
             "moe_workspace_check": (_i32, [_vp, _sz, _i32, _vp]),
+            "moe_backward_workspace_size": (_i32, [P(Config), _i32, P(_sz)]),
+            "moe_backward": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp, _vp, _vp,
+                                    P(FfnGrads), P(FfnGrads), _vp, _sz, _vp]),
             "moe_route_dispatch": (_i32, [P(Config), _vp, _i32, P(Norm), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _sz, _vp]),
             "moe_forward_norm": (_i32, [P(Config), _vp, _i32, P(Norm), _vp, _vp, P(FfnWeights), P(FfnWeights), _vp,
@@ -89,7 +96,7 @@ def _lib():
 
 
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_forward", "moe_forward_norm", "moe_route_dispatch", "moe_forward_noalloc", "moe_workspace_check", "moe_debug_ws_offset",
+           "moe_combine", "moe_forward", "moe_backward", "moe_backward_workspace_size", "moe_forward_norm", "moe_route_dispatch", "moe_forward_noalloc", "moe_workspace_check", "moe_debug_ws_offset",
            "moe_debug_ffn_tile_rows", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
            "moe_debug_trace_count", "moe_debug_trace_name")
 
@@ -211,6 +218,27 @@ def forward_norm(cfg, h, norm, w_router, bias, routed, shared, out, ids, w, x_ou
                                    _ptr(bias), ctypes.byref(routed), None if shared is None else ctypes.byref(shared),
                                    _ptr(out), _ptr(ids), _ptr(w), _ptr(x_out), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_forward_norm")
+
+
+def make_grads(gate, up, down):
+    g = FfnGrads(gate.data_ptr(), up.data_ptr(), down.data_ptr())
+    g._keep = (gate, up, down)
+    return g
+
+
+def backward_workspace_size(cfg, max_tokens):
+    n = ctypes.c_size_t(0)
+    _check(_lib().moe_backward_workspace_size(ctypes.byref(cfg), int(max_tokens), ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return n.value
+
+
+def backward(cfg, x, w_router, bias, routed, shared, dy, dx, d_router, d_bias, d_routed, d_shared, ws, stream=None):
+    """routed/shared: FfnWeights; d_routed/d_shared: FfnGrads (d_shared None without a shared expert)."""
+    _check(_lib().moe_backward(ctypes.byref(cfg), _ptr(x), x.shape[0], _ptr(w_router), _ptr(bias), ctypes.byref(routed),
+                               None if shared is None else ctypes.byref(shared), _ptr(dy), _ptr(dx), _ptr(d_router),
+                               _ptr(d_bias), ctypes.byref(d_routed), None if d_shared is None else ctypes.byref(d_shared),
+                               _ptr(ws), ws.numel(), _stream(stream)), "moe_backward")
 
 
 def forward_noalloc(cfg, x, w_router, bias, routed, shared, out, ids, w, stream=None):

@@ -728,6 +728,194 @@ void* scratch_for(hipStream_t stream) {
   return p;
 }
 
+// ------------------------------------------------------------------ backward
+struct BwdWs {
+  size_t logits, ids, w, off, perm, inv, hist, tiles, ntiles, tiles64, ntiles64;
+  size_t G, U, h, Y, dw, dY, dh, dg, du, dXr;
+  size_t Gs, Us, hs, dhs, dgs, dus, dXs;
+  size_t dl, dlb, dXw;
+  size_t total;
+};
+
+BwdWs bwd_plan(const moe_config* c, int Tm) {
+  const size_t T = size_t(std::max(Tm, 1)), K = c->topk, E = c->n_experts, H = c->hidden, I = c->inter,
+               Is = c->shared_inter, TK = T * K;
+  BwdWs s{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up(std::max<size_t>(bytes, 16));
+    return at;
+  };
+  s.logits = take(T * E * 4);
+  s.ids = take(TK * 4);
+  s.w = take(TK * 4);
+  s.off = take((E + 1) * 4);
+  s.perm = take(TK * 4);
+  s.inv = take(TK * 4);
+  s.hist = take(permute_hist_ints(int(TK), int(E)) * 4);
+  s.tiles = take(size_t(2) * max_tiles(int(TK), int(E), kGemmBM) * 4);
+  s.ntiles = take(16);
+  s.tiles64 = take(size_t(2) * max_tiles(int(TK), int(E), kBwdTileRows) * 4);
+  s.ntiles64 = take(16);
+  s.G = take(TK * I * 4);
+  s.U = take(TK * I * 4);
+  s.h = take(TK * I * 2);
+  s.Y = take(TK * H * 4);
+  s.dw = take(TK * 4);
+  s.dY = take(TK * H * 2);
+  s.dh = take(TK * I * 4);
+  s.dg = take(TK * I * 2);
+  s.du = take(TK * I * 2);
+  s.dXr = take(TK * H * 4);
+  if (Is) {
+    s.Gs = take(T * Is * 4);
+    s.Us = take(T * Is * 4);
+    s.hs = take(T * Is * 2);
+    s.dhs = take(T * Is * 4);
+    s.dgs = take(T * Is * 2);
+    s.dus = take(T * Is * 2);
+    s.dXs = take(T * H * 4);
+  }
+  s.dl = take(T * E * 4);
+  s.dlb = take(T * E * 2);
+  s.dXw = take(T * H * 4);
+  s.total = o;
+  return s;
+}
+
+bool bwd_supported(const moe_config* c) {
+  return c->routed_wfmt == W_BF16 && c->routed_afmt == A_NONE &&
+         (c->shared_inter == 0 || (c->shared_wfmt == W_BF16 && c->shared_afmt == A_NONE));
+}
+
+// the recomputed forward of one FFN on rows already laid out (routed: per
+// segment, gathered from x through perm / K; shared: all T rows): G, U fp32,
+// h = SiLU(G) U bf16, and (routed) Y = h Wd^T fp32
+moe_status bwd_ffn_forward(const moe_config* c, bool routed, const uint16_t* x, int rows, const int* perm,
+                           const int* off, const int* tiles, const int* ntiles, const moe_ffn_weights* W, float* G,
+                           float* U, uint16_t* h, float* Y, hipStream_t s) {
+  hipStream_t s_ = s;
+  const int H = c->hidden, I = routed ? c->inter : c->shared_inter, E = c->n_experts;
+  for (int k = 0; k < 2; ++k) {
+    GemmParams g{};
+    g.A = x;
+    g.lda = H;
+    g.a_map = routed ? perm : nullptr;
+    g.a_div = routed ? c->topk : 1;
+    g.B0 = k ? W->up : W->gate;
+    g.b_stride = long(I) * H;
+    g.N = I;
+    g.K = H;
+    g.seg = routed ? off : nullptr;
+    g.M = rows;
+    g.tiles = routed ? tiles : nullptr;
+    g.ntiles = routed ? ntiles : nullptr;
+    g.max_tiles = routed ? max_tiles(rows, E, kGemmBM) : 0;
+    g.bm = kGemmBM;
+    g.C = k ? U : G;
+    g.ldc = I;
+    LAUNCH(k ? "bwd_up_fwd" : "bwd_gate_fwd", launch_gemm(W_BF16, EPI_F32, g, s));
+  }
+  LAUNCH("bwd_swiglu_fwd", launch_swiglu_fwd(G, U, long(rows) * I, h, s));
+  if (Y) {
+    GemmParams d{};
+    d.A = h;
+    d.lda = I;
+    d.B0 = W->down;
+    d.b_stride = long(H) * I;
+    d.N = H;
+    d.K = I;
+    d.seg = off;
+    d.M = rows;
+    d.tiles = tiles;
+    d.ntiles = ntiles;
+    d.max_tiles = max_tiles(rows, E, kGemmBM);
+    d.bm = kGemmBM;
+    d.C = Y;
+    d.ldc = H;
+    LAUNCH("bwd_down_fwd", launch_gemm(W_BF16, EPI_F32, d, s));
+  }
+  return MOE_OK;
+}
+
+// dh, then dg / du, then dX (two passes) and the three weight gradients of
+// one FFN, from dY (bf16, rows laid out as the FFN's rows)
+moe_status bwd_ffn_backward(const moe_config* c, bool routed, const uint16_t* x, int rows, const int* perm,
+                            const int* off, const int* tiles64, const int* ntiles64, const moe_ffn_weights* W,
+                            const moe_ffn_grads* D, const float* G, const float* U, const uint16_t* h,
+                            const uint16_t* dY, float* dh, uint16_t* dg, uint16_t* du, float* dX, hipStream_t s) {
+  hipStream_t s_ = s;
+  const int H = c->hidden, I = routed ? c->inter : c->shared_inter, E = c->n_experts;
+  const int ngroups = routed ? E : 1;
+  BwdGemmParams n{};  // dh = dY Wd: A = dY [rows][H], B = Wd [H][I]
+  n.A0 = dY;
+  n.lda = H;
+  n.B0 = static_cast<const uint16_t*>(W->down);
+  n.ldb = I;
+  n.b_stride = long(H) * I;
+  n.npass = 1;
+  n.N = I;
+  n.K = H;
+  n.rows = rows;
+  n.seg = routed ? off : nullptr;
+  n.tiles = routed ? tiles64 : nullptr;
+  n.ntiles = routed ? ntiles64 : nullptr;
+  n.max_tiles = routed ? max_tiles(rows, E, kBwdTileRows) : 0;
+  n.C = dh;
+  n.ldc = I;
+  LAUNCH("bwd_dh", launch_bwd_gemm(false, false, n, 1, s));
+  LAUNCH("bwd_swiglu", launch_swiglu_bwd(G, U, dh, long(rows) * I, dg, du, s));
+  BwdGemmParams x2 = n;  // dX = dg Wg + du Wu: A = dg / du [rows][I], B = Wg / Wu [I][H]
+  x2.A0 = dg;
+  x2.A1 = du;
+  x2.lda = I;
+  x2.B0 = static_cast<const uint16_t*>(W->gate);
+  x2.B1 = static_cast<const uint16_t*>(W->up);
+  x2.ldb = H;
+  x2.b_stride = long(I) * H;
+  x2.npass = 2;
+  x2.N = H;
+  x2.K = I;
+  x2.K1 = I;
+  x2.C = dX;
+  x2.ldc = H;
+  LAUNCH("bwd_dx", launch_bwd_gemm(false, false, x2, 1, s));
+  BwdGemmParams t{};  // dWd[e] = dY_e^T h_e: P = dY [rows][H], Q = h [rows][I]
+  t.A0 = dY;
+  t.lda = H;
+  t.B0 = h;
+  t.ldb = I;
+  t.npass = 1;
+  t.M = H;
+  t.N = I;
+  t.rows = rows;
+  t.seg = routed ? off : nullptr;
+  t.C = D->down;
+  t.ldc = I;
+  t.c_stride = long(H) * I;
+  LAUNCH("bwd_ddown", launch_bwd_gemm(true, true, t, ngroups, s));
+  for (int k = 0; k < 2; ++k) {  // dWg[e] = dg_e^T X_e, dWu[e] = du_e^T X_e: P = dg / du [rows][I], Q = x rows
+    BwdGemmParams q{};
+    q.A0 = k ? du : dg;
+    q.lda = I;
+    q.B0 = x;
+    q.ldb = H;
+    q.b_map = routed ? perm : nullptr;
+    q.b_div = routed ? c->topk : 1;
+    q.npass = 1;
+    q.M = I;
+    q.N = H;
+    q.rows = rows;
+    q.seg = routed ? off : nullptr;
+    q.C = k ? D->up : D->gate;
+    q.ldc = H;
+    q.c_stride = long(I) * H;
+    LAUNCH(k ? "bwd_dup" : "bwd_dgate", launch_bwd_gemm(true, true, q, ngroups, s));
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -950,6 +1138,124 @@ moe_status moe_route_dispatch(const moe_config* cfg, const uint16_t* h, int32_t 
   }
   return route_dispatch(cfg, h, T, nm, w_router, bias, topk_ids, topk_w, expert_offsets, perm_src, inv_pos, x_out, xq,
                         xq_scale, nullptr, nullptr, 0, ws, L, stream);
+}
+
+moe_status moe_backward_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes) {
+  if (!bytes || max_tokens < 0) return MOE_EINVAL;
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bwd_supported(cfg)) return MOE_EUNSUPPORTED;
+  *bytes = bwd_plan(cfg, max_tokens).total;
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,
+                        const float* bias, const moe_ffn_weights* routed, const moe_ffn_weights* shared,
+                        const uint16_t* dy, uint16_t* dx, uint16_t* d_router, float* d_bias,
+                        const moe_ffn_grads* d_routed, const moe_ffn_grads* d_shared, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  hipStream_t s_ = stream;
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bwd_supported(cfg)) return MOE_EUNSUPPORTED;
+  if (T < 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  const bool has_shared = cfg->shared_inter > 0;
+  if (!x || !w_router || !routed || !dy || !dx || !d_router || !d_routed || !ws) return MOE_EINVAL;
+  if (!d_routed->gate || !d_routed->up || !d_routed->down) return MOE_EINVAL;
+  if (has_shared && (!shared || !d_shared || !d_shared->gate || !d_shared->up || !d_shared->down)) return MOE_EINVAL;
+  if ((st = check_weights(routed, W_BF16)) != MOE_OK) return st;
+  if (has_shared && (st = check_weights(shared, W_BF16)) != MOE_OK) return st;
+  for (const void* p : {(const void*)x, (const void*)w_router, (const void*)dy, (const void*)dx, (const void*)d_router,
+                        (const void*)ws, (const void*)d_routed->gate, (const void*)d_routed->up,
+                        (const void*)d_routed->down})
+    if (!aligned16(p)) return MOE_EALIGN;
+  const BwdWs L = bwd_plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const int H = cfg->hidden, K = cfg->topk, E = cfg->n_experts, TK = T * K;
+  int* ids = at<int>(ws, L.ids);
+  float* w = at<float>(ws, L.w);
+  int* off = at<int>(ws, L.off);
+  int* perm = at<int>(ws, L.perm);
+  int* inv = at<int>(ws, L.inv);
+  float* logits = at<float>(ws, L.logits);
+  // routing again (the forward's: fp32 logits, then the same top-k), with the
+  // logits kept for the softmax backward
+  {
+    GemmParams g{};
+    g.A = x;
+    g.lda = H;
+    g.B0 = w_router;
+    g.N = E;
+    g.K = H;
+    g.M = T;
+    g.C = logits;
+    g.ldc = E;
+    LAUNCH("bwd_router_logits", launch_gemm(W_BF16, EPI_F32, g, stream));
+    LAUNCH("bwd_topk", launch_topk(logits, T, bias, route_params(cfg), ids, w, stream));
+  }
+  LAUNCH("bwd_permute", launch_permute(ids, TK, E, at<int>(ws, L.hist), off, perm, inv, at<int>(ws, L.tiles),
+                                       at<int>(ws, L.ntiles), kGemmBM, stream));
+  LAUNCH("bwd_tiles64", launch_build_tiles(off, E, TK, kBwdTileRows, at<int>(ws, L.tiles64), at<int>(ws, L.ntiles64),
+                                           stream));
+  // routed experts: recomputed forward, combine backward, FFN backward
+  if ((st = bwd_ffn_forward(cfg, true, x, TK, perm, off, at<int>(ws, L.tiles), at<int>(ws, L.ntiles), routed,
+                            at<float>(ws, L.G), at<float>(ws, L.U), at<uint16_t>(ws, L.h), at<float>(ws, L.Y),
+                            stream)) != MOE_OK)
+    return st;
+  float* dw = at<float>(ws, L.dw);
+  LAUNCH("bwd_combine", launch_combine_bwd(dy, at<float>(ws, L.Y), inv, w, T, K, H, dw, at<uint16_t>(ws, L.dY), stream));
+  if ((st = bwd_ffn_backward(cfg, true, x, TK, perm, off, at<int>(ws, L.tiles64), at<int>(ws, L.ntiles64), routed,
+                             d_routed, at<float>(ws, L.G), at<float>(ws, L.U), at<uint16_t>(ws, L.h),
+                             at<uint16_t>(ws, L.dY), at<float>(ws, L.dh), at<uint16_t>(ws, L.dg), at<uint16_t>(ws, L.du),
+                             at<float>(ws, L.dXr), stream)) != MOE_OK)
+    return st;
+  // shared expert: dY = dy on every token
+  float* dXs = nullptr;
+  if (has_shared) {
+    if ((st = bwd_ffn_forward(cfg, false, x, T, nullptr, nullptr, nullptr, nullptr, shared, at<float>(ws, L.Gs),
+                              at<float>(ws, L.Us), at<uint16_t>(ws, L.hs), nullptr, stream)) != MOE_OK)
+      return st;
+    dXs = at<float>(ws, L.dXs);
+    if ((st = bwd_ffn_backward(cfg, false, x, T, nullptr, nullptr, nullptr, nullptr, shared, d_shared,
+                               at<float>(ws, L.Gs), at<float>(ws, L.Us), at<uint16_t>(ws, L.hs), dy,
+                               at<float>(ws, L.dhs), at<uint16_t>(ws, L.dgs), at<uint16_t>(ws, L.dus), dXs, stream)) !=
+        MOE_OK)
+      return st;
+  }
+  // router: softmax backward, d_router = dl^T x, dx += dl Wr, d_bias = sum dl
+  float* dl = at<float>(ws, L.dl);
+  uint16_t* dlb = at<uint16_t>(ws, L.dlb);
+  LAUNCH("bwd_router", launch_router_bwd(logits, bias, ids, dw, T, E, K, cfg->route_scale, dl, dlb, stream));
+  {
+    BwdGemmParams t{};
+    t.A0 = dlb;
+    t.lda = E;
+    t.B0 = x;
+    t.ldb = H;
+    t.npass = 1;
+    t.M = E;
+    t.N = H;
+    t.rows = T;
+    t.C = d_router;
+    t.ldc = H;
+    LAUNCH("bwd_drouter", launch_bwd_gemm(true, true, t, 1, stream));
+    BwdGemmParams n{};
+    n.A0 = dlb;
+    n.lda = E;
+    n.B0 = w_router;
+    n.ldb = H;
+    n.npass = 1;
+    n.N = H;
+    n.K = E;
+    n.rows = T;
+    n.C = at<float>(ws, L.dXw);
+    n.ldc = H;
+    LAUNCH("bwd_dx_router", launch_bwd_gemm(false, false, n, 1, stream));
+  }
+  if (d_bias) LAUNCH("bwd_dbias", launch_colsum(dl, T, E, d_bias, stream));
+  LAUNCH("bwd_dx_sum", launch_dx_sum(at<float>(ws, L.dXr), inv, K, dXs, at<float>(ws, L.dXw), T, H, dx, stream));
+  return MOE_OK;
 }
 
 moe_status moe_forward_noalloc(const moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w_router,

@@ -239,6 +239,51 @@ hipError_t launch_combine(const void* y_perm, bool y_bf16, const int* inv_pos, c
                           const void* y_shared, bool ys_bf16, int T, int K, int H, uint16_t* out,
                           hipStream_t s);
 
+// ------------------------------------------------------------------ backward (backward.hip)
+// C (+)= sum_k A(m, k) B(k, n), bf16 operands, fp32 accumulate, 64 x 64 tiles.
+//   NN (tn false): rows m of the groups' segments (tile list of 64-row tiles,
+//     or rows 0..rows-1 of one group), A[m][k] row-major (row gathered through
+//     a_map[seg0 + m] / a_div when set), B of group e at B + e * b_stride
+//     stored [k][n]; npass = 2 adds A1 (K1 columns) times B1.  C rows are the
+//     A rows: C[(seg0 + m) * ldc + n].
+//   TN (tn true): per group e, C_e[m][n] = sum over the group's segment rows
+//     k of P[k][m] Q[k][n]; P = A0 (row k at a_map[k] / a_div when set), Q = B0
+//     (row k at b_map[k] / b_div when set); C_e at C + e * c_stride.  Without
+//     seg, one group over rows 0..rows-1.
+struct BwdGemmParams {
+  const uint16_t* A0;
+  const uint16_t* A1;
+  long lda;
+  const int* a_map;
+  int a_div;
+  const uint16_t* B0;
+  const uint16_t* B1;
+  long ldb, b_stride;
+  const int* b_map;
+  int b_div;
+  int npass;
+  int M, N, K, K1;
+  int rows;
+  const int* seg;
+  const int* tiles;
+  const int* ntiles;
+  int max_tiles;
+  void* C;
+  long ldc, c_stride;
+};
+constexpr int kBwdTileRows = 64;
+hipError_t launch_bwd_gemm(bool tn, bool out_bf16, const BwdGemmParams& p, int n_groups, hipStream_t s);
+hipError_t launch_swiglu_fwd(const float* g, const float* u, long n, uint16_t* h, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, long n, uint16_t* dg, uint16_t* du,
+                             hipStream_t s);
+hipError_t launch_combine_bwd(const uint16_t* dy, const float* Y, const int* inv_pos, const float* w, int T, int K,
+                              int H, float* dw, uint16_t* dY, hipStream_t s);
+hipError_t launch_router_bwd(const float* logits, const float* bias, const int* ids, const float* dw, int T, int E,
+                             int K, float scale, float* dl, uint16_t* dl_bf, hipStream_t s);
+hipError_t launch_dx_sum(const float* dXr, const int* inv_pos, int K, const float* dXs, const float* dXw, int T, int H,
+                         uint16_t* dx, hipStream_t s);
+hipError_t launch_colsum(const float* dl, int T, int E, float* out, hipStream_t s);
+
 // ------------------------------------------------------------------ diagnostics
 hipError_t launch_e4m3_decode(const uint8_t* codes, float* out, int n, hipStream_t s);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* codes, int n, hipStream_t s);
