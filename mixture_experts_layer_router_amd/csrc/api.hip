@@ -730,7 +730,7 @@ void* scratch_for(hipStream_t stream) {
 
 // ------------------------------------------------------------------ backward
 struct BwdWs {
-  size_t logits, ids, w, off, perm, inv, hist, tiles, ntiles, tiles64, ntiles64;
+  size_t logits, ids, w, off, perm, inv, hist, tiles, ntiles;
   size_t G, U, h, Y, dw, dY, dh, dg, du, dXr;
   size_t Gs, Us, hs, dhs, dgs, dus, dXs;
   size_t dl, dlb, dXw;
@@ -756,8 +756,6 @@ BwdWs bwd_plan(const moe_config* c, int Tm) {
   s.hist = take(permute_hist_ints(int(TK), int(E)) * 4);
   s.tiles = take(size_t(2) * max_tiles(int(TK), int(E), kGemmBM) * 4);
   s.ntiles = take(16);
-  s.tiles64 = take(size_t(2) * max_tiles(int(TK), int(E), kBwdTileRows) * 4);
-  s.ntiles64 = take(16);
   s.G = take(TK * I * 4);
   s.U = take(TK * I * 4);
   s.h = take(TK * I * 2);
@@ -842,7 +840,7 @@ moe_status bwd_ffn_forward(const moe_config* c, bool routed, const uint16_t* x, 
 // dh, then dg / du, then dX (two passes) and the three weight gradients of
 // one FFN, from dY (bf16, rows laid out as the FFN's rows)
 moe_status bwd_ffn_backward(const moe_config* c, bool routed, const uint16_t* x, int rows, const int* perm,
-                            const int* off, const int* tiles64, const int* ntiles64, const moe_ffn_weights* W,
+                            const int* off, const int* tiles, const int* ntiles, const moe_ffn_weights* W,
                             const moe_ffn_grads* D, const float* G, const float* U, const uint16_t* h,
                             const uint16_t* dY, float* dh, uint16_t* dg, uint16_t* du, float* dX, hipStream_t s) {
   hipStream_t s_ = s;
@@ -859,9 +857,9 @@ moe_status bwd_ffn_backward(const moe_config* c, bool routed, const uint16_t* x,
   n.K = H;
   n.rows = rows;
   n.seg = routed ? off : nullptr;
-  n.tiles = routed ? tiles64 : nullptr;
-  n.ntiles = routed ? ntiles64 : nullptr;
-  n.max_tiles = routed ? max_tiles(rows, E, kBwdTileRows) : 0;
+  n.tiles = routed ? tiles : nullptr;  // 128-row tiles (the forward's list)
+  n.ntiles = routed ? ntiles : nullptr;
+  n.max_tiles = routed ? max_tiles(rows, E, kGemmBM) : 0;
   n.C = dh;
   n.ldc = I;
   LAUNCH("bwd_dh", launch_bwd_gemm(false, false, n, 1, s));
@@ -1196,8 +1194,6 @@ moe_status moe_backward(const moe_config* cfg, const uint16_t* x, int32_t T, con
   }
   LAUNCH("bwd_permute", launch_permute(ids, TK, E, at<int>(ws, L.hist), off, perm, inv, at<int>(ws, L.tiles),
                                        at<int>(ws, L.ntiles), kGemmBM, stream));
-  LAUNCH("bwd_tiles64", launch_build_tiles(off, E, TK, kBwdTileRows, at<int>(ws, L.tiles64), at<int>(ws, L.ntiles64),
-                                           stream));
   // routed experts: recomputed forward, combine backward, FFN backward
   if ((st = bwd_ffn_forward(cfg, true, x, TK, perm, off, at<int>(ws, L.tiles), at<int>(ws, L.ntiles), routed,
                             at<float>(ws, L.G), at<float>(ws, L.U), at<uint16_t>(ws, L.h), at<float>(ws, L.Y),
@@ -1205,7 +1201,7 @@ moe_status moe_backward(const moe_config* cfg, const uint16_t* x, int32_t T, con
     return st;
   float* dw = at<float>(ws, L.dw);
   LAUNCH("bwd_combine", launch_combine_bwd(dy, at<float>(ws, L.Y), inv, w, T, K, H, dw, at<uint16_t>(ws, L.dY), stream));
-  if ((st = bwd_ffn_backward(cfg, true, x, TK, perm, off, at<int>(ws, L.tiles64), at<int>(ws, L.ntiles64), routed,
+  if ((st = bwd_ffn_backward(cfg, true, x, TK, perm, off, at<int>(ws, L.tiles), at<int>(ws, L.ntiles), routed,
                              d_routed, at<float>(ws, L.G), at<float>(ws, L.U), at<uint16_t>(ws, L.h),
                              at<uint16_t>(ws, L.dY), at<float>(ws, L.dh), at<uint16_t>(ws, L.dg), at<uint16_t>(ws, L.du),
                              at<float>(ws, L.dXr), stream)) != MOE_OK)

@@ -197,6 +197,201 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemmParams p) {
       }
 }
 
+// ---------------------------------------------------------------------------
+// bwd_gemm_tr_kernel: the same two shapes on 128 x 128 tiles, 32-deep K steps,
+// 4 waves x 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Operands stay in LDS in
+// the layout they have in memory: a k-contiguous operand (NN's A) as
+// [row][k], a k-major one (NN's B, both TN operands) as [k][row], whose MFMA
+// fragments (8 consecutive k of one row per lane) come from two transposing
+// LDS reads (ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the 8 bytes read by lane 4 j + i / 4 as its element j, so
+// lanes that point at [kb + s/4][rb + 4 (s%4)] give lane i rows rb + i at
+// k = kb .. kb+3).  The next step's tiles are loaded into registers while
+// the current step's MFMAs run, then stored into the other LDS buffer: one
+// barrier per step.  Requires every leading dimension, K (NN) and the
+// row/column counts to be multiples of 8 (16-byte loads); the launcher
+// falls back to bwd_gemm_kernel otherwise.
+constexpr int TT = 128, TK = 32;
+constexpr int KCP = TK + 8;   // bf16 per row of a [row][k] tile (80 bytes: 16-byte reads spread over banks)
+constexpr int RCP = TT + 16;  // bf16 per k-row of a [k][row] tile (288 bytes)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// thread's 32 bytes of a [row][k] tile: row t/2, k 16 (t%2) + [0, 16)
+template <class RowMap>
+MOE_DEV void kc_load(u32x4 (&v)[2], const uint16_t* src, long ld, int nrow, int k0, int K, RowMap row_phys) {
+  const int t = threadIdx.x, r = t >> 1;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int kk = k0 + 16 * (t & 1) + 8 * q;
+    v[q] = (r < nrow && kk < K) ? *reinterpret_cast<const u32x4*>(src + row_phys(r) * ld + kk) : u32x4{0, 0, 0, 0};
+  }
+}
+MOE_DEV void kc_store(uint16_t* tile, const u32x4 (&v)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4*>(tile + (t >> 1) * KCP + 16 * (t & 1) + 8 * q) = v[q];
+}
+// thread's 32 bytes of a [k][row] tile: k t/8, rows 16 (t%8) + [0, 16) (row0..row0+127 of the source)
+template <class KMap>
+MOE_DEV void rc_load(u32x4 (&v)[2], const uint16_t* src, long ld, int row0, int nrow, int k, int kend, KMap k_phys) {
+  const int t = threadIdx.x, kr = k + (t >> 3);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * (t & 7) + 8 * q;
+    v[q] = (kr < kend && row0 + r < nrow) ? *reinterpret_cast<const u32x4*>(src + k_phys(kr) * ld + row0 + r)
+                                          : u32x4{0, 0, 0, 0};
+  }
+}
+MOE_DEV void rc_store(uint16_t* tile, const u32x4 (&v)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4*>(tile + (t >> 3) * RCP + 16 * (t & 7) + 8 * q) = v[q];
+}
+// MFMA fragment (rows rb + lane % 32, k = 16 h + 8 (lane / 32) + [0, 8)) of a [row][k] tile
+MOE_DEV bf16x8_b kc_frag(const uint16_t* tile, int rb, int h) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8_b*>(tile + (rb + (l & 31)) * KCP + 16 * h + 8 * (l >> 5));
+}
+// ... of a [k][row] tile, by two transposing reads
+MOE_DEV bf16x8_b rc_frag(const uint16_t* tile, int rb, int h) {
+  const int l = lane_id(), gg = l >> 4, sl = l & 15;
+  const uint16_t* base = tile + (16 * h + 8 * (gg >> 1) + (sl >> 2)) * RCP + rb + 16 * (gg & 1) + 4 * (sl & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(base));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(base + 4 * RCP));
+  const short e[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_b, e);
+}
+
+template <bool TN, bool OUT_BF16>
+__global__ __launch_bounds__(256) void bwd_gemm_tr_kernel(BwdGemmParams p) {
+  // NN: A [row][k] (TT x KCP), B [k][n] (TK x RCP); TN: both [k][row]
+  constexpr int A_ELEMS = TN ? TK * RCP : TT * KCP;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][A_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TK * RCP];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int NB = (p.N + TT - 1) / TT;
+  int e = 0, m0, n0, rows, seg0 = 0;
+  long kbeg = 0, kend = p.K;
+  if constexpr (TN) {
+    const int MB = (p.M + TT - 1) / TT;
+    const int per = MB * NB;
+    e = blockIdx.x / per;
+    const int rest = blockIdx.x % per;
+    m0 = (rest / NB) * TT;
+    n0 = (rest % NB) * TT;
+    rows = p.M;
+    if (p.seg) {
+      kbeg = min(max(p.seg[e], 0), p.rows);
+      kend = min(max(p.seg[e + 1], int(kbeg)), p.rows);
+    } else {
+      kend = p.rows;
+    }
+  } else {
+    const int tix = blockIdx.x / NB;
+    n0 = (blockIdx.x % NB) * TT;
+    if (p.tiles) {
+      if (tix >= p.ntiles[0]) return;
+      e = p.tiles[2 * tix];
+      m0 = p.tiles[2 * tix + 1];
+      seg0 = min(max(p.seg[e], 0), p.rows);
+      const int seg1 = min(max(p.seg[e + 1], seg0), p.rows);
+      rows = seg1 - seg0;
+    } else {
+      m0 = tix * TT;
+      rows = p.rows;
+    }
+    if (m0 >= rows) return;
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  for (int pass = 0; pass < p.npass; ++pass) {
+    const uint16_t* A = pass ? p.A1 : p.A0;
+    const uint16_t* B = pass ? p.B1 : p.B0;
+    const uint16_t* Bg = TN ? B : B + long(e) * p.b_stride;
+    const int* amap = p.a_map;
+    const int adiv = p.a_div;
+    const int* bmap = p.b_map;
+    const int bdiv = p.b_div;
+    // NN: A rows of the segment (optionally gathered); TN: source rows of the k index
+    auto a_row = [&](int r) -> long {
+      const long q = seg0 + m0 + r;
+      return amap ? long(amap[q] / adiv) : q;
+    };
+    auto ka = [&](int k) -> long { return amap ? long(amap[k] / adiv) : k; };
+    auto kb = [&](int k) -> long { return bmap ? long(bmap[k] / bdiv) : k; };
+    auto kid = [](int k) -> long { return k; };
+    const int Kp = TN ? int(kend - kbeg) : (pass ? p.K1 : p.K);
+    const int nsteps = (Kp + TK - 1) / TK;
+    if (nsteps <= 0) continue;
+    u32x4 ra[2], rb[2];
+    auto load = [&](int st) {
+      const int k = st * TK;
+      if constexpr (TN) {
+        rc_load(ra, A, p.lda, m0, p.M, int(kbeg) + k, int(kend), ka);
+        rc_load(rb, B, p.ldb, n0, p.N, int(kbeg) + k, int(kend), kb);
+      } else {
+        kc_load(ra, A, p.lda, rows - m0, k, Kp, a_row);
+        rc_load(rb, Bg, p.ldb, n0, p.N, k, Kp, kid);
+      }
+    };
+    auto store = [&](int buf) {
+      if constexpr (TN) rc_store(sA[buf], ra);
+      else kc_store(sA[buf], ra);
+      rc_store(sB[buf], rb);
+    };
+    __syncthreads();  // the previous pass's last reads of both buffers are done
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+      const int buf = st & 1;
+      const bool more = st + 1 < nsteps;
+      if (more) load(st + 1);
+#pragma unroll
+      for (int h = 0; h < TK / 16; ++h) {
+        bf16x8_b a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[i] = TN ? rc_frag(sA[buf], 64 * wm + 32 * i, h) : kc_frag(sA[buf], 64 * wm + 32 * i, h);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = rc_frag(sB[buf], 64 * wn + 32 * j, h);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+      if (more) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // lane l: column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4 of each 32 x 32 block
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int n = n0 + 64 * wn + 32 * j + l32;
+        if (m >= rows || n >= p.N) continue;
+        const long off = TN ? long(e) * p.c_stride + long(m) * p.ldc + n : (long(seg0) + m) * p.ldc + n;
+        if constexpr (OUT_BF16)
+          static_cast<uint16_t*>(p.C)[off] = f32_to_bf16(acc[i][j][r]);
+        else
+          static_cast<float*>(p.C)[off] = acc[i][j][r];
+      }
+}
+
 MOE_DEV float sig(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
 __global__ void swiglu_fwd_kernel(const float* __restrict__ g, const float* __restrict__ u, long n,
@@ -298,25 +493,45 @@ __global__ void dx_sum_kernel(const float* __restrict__ dXr, const int* __restri
   dx[i] = f32_to_bf16(v);
 }
 
-// out[e] = sum over t of dl[t][e], in token order
-__global__ void colsum_kernel(const float* __restrict__ dl, int T, int E, float* __restrict__ out) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= E) return;
+// out[e] = sum over t of dl[t][e]: one workgroup per expert; thread i sums
+// tokens i, i + 256, ... in order, then a fixed-order tree over the threads
+__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ dl, int T, int E, float* __restrict__ out) {
+  __shared__ float part[256];
+  const int e = blockIdx.x;
   float v = 0.f;
-  for (int t = 0; t < T; ++t) v += dl[size_t(t) * E + e];
-  out[e] = v;
+  for (int t = threadIdx.x; t < T; t += 256) v += dl[size_t(t) * E + e];
+  part[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (int(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[e] = part[0];
 }
 
 }  // namespace
 
 hipError_t launch_bwd_gemm(bool tn, bool out_bf16, const BwdGemmParams& p, int n_groups, hipStream_t s) {
-  const long NB = (p.N + BN - 1) / BN;
+  // the 128 x 128 transposing-read kernel needs 16-byte aligned rows everywhere
+  const bool tr = p.lda % 8 == 0 && p.ldb % 8 == 0 && p.N % 8 == 0 && p.b_stride % 8 == 0 &&
+                  (tn ? p.M % 8 == 0 : (p.K % 8 == 0 && (p.npass < 2 || p.K1 % 8 == 0)));
+  if (p.tiles && !tr) return hipErrorInvalidValue;  // tile lists hold 128-row tiles
+  const int tile = tr ? TT : BM;
+  const long NB = (p.N + tile - 1) / tile;
   long blocks;
-  if (tn) blocks = long(n_groups) * ((p.M + BM - 1) / BM) * NB;
-  else blocks = (p.tiles ? long(p.max_tiles) : long((p.rows + BM - 1) / BM)) * NB;
+  if (tn) blocks = long(n_groups) * ((p.M + tile - 1) / tile) * NB;
+  else blocks = (p.tiles ? long(p.max_tiles) : long((p.rows + tile - 1) / tile)) * NB;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(blocks));
-  if (tn) {
+  if (tr) {
+    if (tn) {
+      if (out_bf16) hipLaunchKernelGGL((bwd_gemm_tr_kernel<true, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((bwd_gemm_tr_kernel<true, false>), grid, dim3(256), 0, s, p);
+    } else {
+      if (out_bf16) hipLaunchKernelGGL((bwd_gemm_tr_kernel<false, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((bwd_gemm_tr_kernel<false, false>), grid, dim3(256), 0, s, p);
+    }
+  } else if (tn) {
     if (out_bf16) hipLaunchKernelGGL((bwd_gemm_kernel<true, true>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((bwd_gemm_kernel<true, false>), grid, dim3(256), 0, s, p);
   } else {
@@ -366,7 +581,7 @@ hipError_t launch_dx_sum(const float* dXr, const int* inv_pos, int K, const floa
 
 hipError_t launch_colsum(const float* dl, int T, int E, float* out, hipStream_t s) {
   if (E <= 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_kernel, dim3(unsigned((E + 255) / 256)), dim3(256), 0, s, dl, T, E, out);
+  hipLaunchKernelGGL(colsum_kernel, dim3(unsigned(E)), dim3(256), 0, s, dl, T, E, out);
   return hipGetLastError();
 }
 

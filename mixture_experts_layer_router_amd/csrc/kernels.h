@@ -271,7 +271,6 @@ struct BwdGemmParams {
   void* C;
   long ldc, c_stride;
 };
-constexpr int kBwdTileRows = 64;
 hipError_t launch_bwd_gemm(bool tn, bool out_bf16, const BwdGemmParams& p, int n_groups, hipStream_t s);
 hipError_t launch_swiglu_fwd(const float* g, const float* u, long n, uint16_t* h, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, long n, uint16_t* dg, uint16_t* du,
