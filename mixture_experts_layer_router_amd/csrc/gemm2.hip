@@ -159,8 +159,11 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
 
   // LDS operand reads: block i of the lane's rows, chunks 4h+g and 4h+2+g
   const int f = (l32 >> 1) & 7;
-  const int rowA = (128 * wm + l32) * RB, rowB = (128 * wn + l32) * RB;
-  const int srowA = (128 * wm + l32) * 16 + g, srowB = (128 * wn + l32) * 16 + g;
+  // the wave's A row blocks interleave with the other row half's: block i
+  // covers tile rows 64 i + 32 wm + [0, 32), so a partial tile's blocks are
+  // shared by both halves
+  const int rowA = (32 * wm + l32) * RB, rowB = (128 * wn + l32) * RB;
+  const int srowA = (32 * wm + l32) * 16 + g, srowB = (128 * wn + l32) * 16 + g;
   constexpr int NR = 16 + (MX ? 8 : 0);  // LDS reads per step
   auto read_op = [&](int r, Frag& fr, int t) {  // read r of step t's operands
     const int buf = (t >> 1) & 1, h = t & 1;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
     const int colo0 = ((4 * h + g) ^ f) << 4, colo1 = ((4 * h + 2 + g) ^ f) << 4;
     if (r < 8) {
       const int i = r / 2;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(As_ + rowA + 32 * RB * i + ((r & 1) ? colo1 : colo0));
+      const i32x4 v = *reinterpret_cast<const i32x4*>(As_ + rowA + 64 * RB * i + ((r & 1) ? colo1 : colo0));
       if (r & 1)
         fr.a[i].hi = v;
       else
@@ -184,14 +187,14 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
     } else if constexpr (MX) {
       const int buf = (t / kSG) % kSBuf, byte = 2 * (t % kSG);
       if (r < 20)
-        fr.sa[r - 16] = sS[buf][0][srowA + 32 * 16 * (r - 16) + byte];
+        fr.sa[r - 16] = sS[buf][0][srowA + 64 * 16 * (r - 16) + byte];
       else
         fr.sb[r - 20] = sS[buf][1][srowB + 32 * 16 * (r - 20) + byte];
     }
   };
 
-  // rows of this wave's blocks that hold valid rows: blocks at or past nI are skipped
-  const int nI = min(max((mrows - 128 * wm + 31) / 32, 0), 4);
+  // this wave's blocks that hold valid rows (block i is tile block 2 i + wm): blocks at or past nI are skipped
+  const int nI = min(max(((mrows + 31) / 32 - wm + 1) / 2, 0), 4);
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
 
   // ------------------------------------------------------------ epilogue
   // lane l holds column l%32 of each 32x32 block, rows 8(r/4) + 4(l/32) + r%4
-  auto row_of = [&](int i, int r) { return 128 * wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3); };
+  auto row_of = [&](int i, int r) { return 64 * i + 32 * wm + 8 * (r >> 2) + 4 * g + (r & 3); };
   if constexpr (EPI == EPI_GATEUP) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int b = lane + 64 * k, row = b >> 1, half = b & 1;
-        const int rl = 128 * wm + 64 * h + row;
+        const int rl = 128 * h + 64 * (row >> 5) + 32 * wm + (row & 31);  // staged block 2 h + row / 32
         f32x4 v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const f32x4*>(wsf + row * RSF + 32 * half + 4 * q);
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
 #pragma unroll 4
       for (int c = lane; c < 32 * CPR; c += 64) {
         const int rl = c / CPR, cc = c % CPR;
-        const int row = 128 * wm + 32 * i + rl;
+        const int row = 64 * i + 32 * wm + rl;
         if (row >= mrows) continue;
         const int col = cw + cc * (16 / ES);
         const i32x4 v = *reinterpret_cast<const i32x4*>(ws + rl * RS + cc * 16);

@@ -74,20 +74,21 @@ MOE_DEV Tile tile_of(const GemmParams& p, int bm, int nper, int ks) {
   if (int(blockIdx.x / 8) >= chunk || idx >= T) return t;
   t.kz = idx % ks;  // K slice (split-K: slices of one tile are adjacent)
   idx /= ks;
-  int e = 0, nb, m0;
+  int e = 0, nb, m0, step = bm;
   {
     const int pe = idx / NB;  // a tile-list entry of the same expert
     int be = 0, ne = nt_list;
     if (p.tiles) {
       e = p.tiles[2 * pe];
-      be = pe - p.tiles[2 * pe + 1] / bm;
       const int c0 = min(max(p.seg[e], 0), p.M), c1 = min(max(p.seg[e + 1], c0), p.M);
+      step = tile_step(c1 - c0, bm);
+      be = pe - p.tiles[2 * pe + 1] / step;
       ne = max((c1 - c0 + bm - 1) / bm, 1);
     }
     const int local = idx - be * NB;
     if (p.tiles) {  // one expert's m-tiles of an n-block are adjacent
       nb = local / ne;
-      m0 = (local % ne) * bm;
+      m0 = (local % ne) * step;
     } else {  // one group: groups of 4 m-tiles, n-block-major within a group
       const int gm = 4, grp = local / (gm * NB), rest = local - grp * gm * NB;
       const int gsz = min(gm, ne - grp * gm);
@@ -102,7 +103,7 @@ MOE_DEV Tile tile_of(const GemmParams& p, int bm, int nper, int ks) {
   t.m0 = m0;
   t.n0 = nb * nper;
   t.seg0 = seg0;
-  t.mrows = min(bm, seg1 - seg0 - m0);
+  t.mrows = min(step, seg1 - seg0 - m0);
   t.valid = t.mrows > 0;
   return t;
 }

@@ -64,6 +64,20 @@ hipError_t launch_permute_scatter(const int* ids, int TK, int E, const int* hist
                                   int* perm_src, int* inv_pos, int* tiles, int* ntiles, int bm, hipStream_t s);
 hipError_t launch_build_tiles(const int* offsets, int E, int rows, int bm, int* tiles, int* ntiles, hipStream_t s);
 inline int max_tiles(int rows, int E, int bm) { return (rows + bm - 1) / bm + E; }
+// Row offset step of one expert's grouped-GEMM tiles: an expert with cnt rows
+// gets ceil(cnt / bm) tiles.  For the 256-row kernel they share the rows
+// evenly in multiples of 32 (one MFMA row block), so 272 rows run as 160 + 112
+// rather than 256 + 16: a tile whose row blocks are spread over both halves of
+// the workgroup's waves takes time in proportion to its blocks, while a
+// 16-row tail costs about half a full tile in its latency-bound K loop.  The
+// 128-row kernel keeps tiles of bm rows (its waves hold 2 blocks each, so an
+// even split gains nothing).  Every tile holds at least one row.
+__host__ __device__ inline int tile_step(int cnt, int bm) {
+  const int n = (cnt + bm - 1) / bm;
+  if (bm < 256 || n <= 1) return bm;
+  const int h = ((cnt + n - 1) / n + 31) / 32 * 32;
+  return (h >= bm || (n - 1) * h >= cnt) ? bm : h;
+}
 
 // ------------------------------------------------------------------ quantisers
 // Row r of the output reads input row (row_map ? row_map[r] / row_div : r).

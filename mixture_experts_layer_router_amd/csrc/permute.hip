@@ -81,10 +81,10 @@ MOE_DEV void write_tiles(const int* cnt, int E, int bm, int* tiles, int* ntiles,
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
-    int n = (cnt[e] + bm - 1) / bm, b = scratch[e];
+    const int n = (cnt[e] + bm - 1) / bm, b = scratch[e], step = tile_step(cnt[e], bm);
     for (int i = 0; i < n; ++i) {
       tiles[2 * (b + i)] = e;
-      tiles[2 * (b + i) + 1] = i * bm;
+      tiles[2 * (b + i) + 1] = i * step;
     }
   }
 }

@@ -288,8 +288,23 @@ def _check_dispatch(cfg, layer, r):
     n = int(moe.ws_region(c, T, layer.ws, "ntiles", 1).cpu().numpy()[0])
     tiles = moe.ws_region(c, T, layer.ws, "tiles", 2 * n).cpu().numpy().reshape(n, 2)
     cnt = np.diff(r.offsets)
-    want = sorted((e, m) for e in range(E) for m in range(0, int(cnt[e]), bm))
+    want = sorted((e, i * _tile_step(int(cnt[e]), bm)) for e in range(E) for i in range(-(-int(cnt[e]) // bm)))
     assert sorted(map(tuple, tiles.tolist())) == want
+    # every row of every segment in exactly one tile
+    for e in range(E):
+        starts = sorted(m for (ee, m) in tiles.tolist() if ee == e)
+        ends = starts[1:] + [int(cnt[e])]
+        assert all(0 <= a < b <= int(cnt[e]) for a, b in zip(starts, ends)) and (not starts or starts[0] == 0)
+
+
+def _tile_step(cnt, bm):
+    """Row offset between one expert's tiles: ceil(cnt/bm) tiles; for 256-row
+    tiles the rows are shared evenly in multiples of 32 (each tile non-empty)."""
+    n = -(-cnt // bm)
+    if bm < 256 or n <= 1:
+        return bm
+    h = (-(-cnt // n) + 31) // 32 * 32
+    return bm if (h >= bm or (n - 1) * h >= cnt) else h
 
 
 @pytest.mark.parametrize("cfgname", [c.name for c in synth.CONFIGS])
