@@ -336,6 +336,22 @@ moe_status moe_debug_ws_offset(const moe_config* cfg /*host*/, int32_t max_token
                                size_t* offset /*host*/);
 int32_t moe_debug_ffn_tile_rows(const moe_config* cfg /*host*/, int32_t which);
 
+/* Debug check of the dispatch that moe_forward's batched path (T > 8) or
+ * moe_route_dispatch left in a workspace planned for T tokens, against the
+ * ids of that call (device, int32 [T][K]): one single-workgroup launch on
+ * `stream` that only reads, and ORs into *flags (device int32; the caller
+ * zeroes it and reads it after synchronising) bit 0 if expert_offsets[0]
+ * != 0 or the offsets decrease, bit 1 if expert_offsets[E] != T*K, bit 2 for
+ * an id outside [0, E), bit 3 if perm_src is not a bijection of [0, T*K) or
+ * inv_pos not its inverse, bit 4 if a position of an expert's segment holds a
+ * slot of another expert or a segment is not in ascending slot order, bit 5
+ * if the grouped-GEMM tile list does not cover each segment in order with
+ * ceil(count / rows) tiles.  These are the properties the grouped GEMMs and
+ * the combine rely on (Mixture-of-Kittens, Figure 1: the dispatch layout the
+ * expert GEMMs consume).  MOE_EINVAL / MOE_EWORKSPACE for bad arguments. */
+moe_status moe_debug_validate_dispatch(const moe_config* cfg /*host*/, int32_t T, const int32_t* topk_ids,
+                                       const void* ws, size_t ws_bytes, int32_t* flags, hipStream_t stream);
+
 /* Measurement hook: arm (events != NULL, n_events >= 2) or disarm (NULL) a
  * launch trace.  While armed, each kernel launch of the entry points records
  * events[2i] before and events[2i+1] after launch i on the call's stream,

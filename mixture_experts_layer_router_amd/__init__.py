@@ -81,6 +81,7 @@ def _lib():
             "moe_forward_noalloc": (_i32, [P(Config), _vp, _i32, _vp, _vp, P(FfnWeights), P(FfnWeights), _vp, _vp,
                                            _vp, _vp]),
             "moe_debug_ws_offset": (_i32, [P(Config), _i32, _i32, P(_sz)]),
+            "moe_debug_validate_dispatch": (_i32, [P(Config), _i32, _vp, _vp, _sz, _vp, _vp]),
             "moe_debug_ffn_tile_rows": (_i32, [P(Config), _i32]),
             "moe_debug_e4m3_decode": (_i32, [_vp, _vp, _i32, _vp]),
             "moe_debug_e4m3_encode": (_i32, [_vp, _vp, _i32, _vp]),
@@ -97,6 +98,7 @@ def _lib():
 
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_combine", "moe_forward", "moe_backward", "moe_backward_workspace_size", "moe_forward_norm", "moe_route_dispatch", "moe_forward_noalloc", "moe_workspace_check", "moe_debug_ws_offset",
+           "moe_debug_validate_dispatch",
            "moe_debug_ffn_tile_rows", "moe_debug_e4m3_decode", "moe_debug_e4m3_encode", "moe_debug_trace",
            "moe_debug_trace_count", "moe_debug_trace_name")
 
@@ -192,6 +194,16 @@ def ws_region(cfg, max_tokens, ws, name, count):
     _check(_lib().moe_debug_ws_offset(ctypes.byref(cfg), int(max_tokens), WS_REGIONS[name], ctypes.byref(off)),
            "moe_debug_ws_offset")
     return ws[off.value:off.value + 4 * count].view(torch.int32)
+
+
+def validate_dispatch(cfg, T, ids, ws, stream=None):
+    """Bit mask of the dispatch checks that fail on the arrays a batched call
+    left in `ws` for the ids `ids` (0: all hold; synchronises the stream)."""
+    flags = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    _check(_lib().moe_debug_validate_dispatch(ctypes.byref(cfg), int(T), _ptr(ids), _ptr(ws), ws.numel(), _ptr(flags),
+                                              _stream(stream)), "moe_debug_validate_dispatch")
+    torch.cuda.synchronize(ws.device)
+    return int(flags.item())
 
 
 def ffn_tile_rows(cfg, which):

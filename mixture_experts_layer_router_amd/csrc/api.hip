@@ -1268,6 +1268,23 @@ moe_status moe_forward_noalloc(const moe_config* cfg, const uint16_t* x, int32_t
                       stream, false);
 }
 
+moe_status moe_debug_validate_dispatch(const moe_config* cfg, int32_t T, const int32_t* topk_ids, const void* ws,
+                                       size_t ws_bytes, int32_t* flags, hipStream_t stream) {
+  hipStream_t s_ = stream;
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (T <= 0 || !topk_ids || !ws || !flags) return MOE_EINVAL;
+  const Ws L = plan(cfg, T);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const int bm = ffn_tile_rows(cfg->routed_wfmt, cfg->hidden, cfg->inter);
+  LAUNCH("validate_dispatch",
+         launch_validate_dispatch(topk_ids, T * cfg->topk, cfg->n_experts, at<int>(const_cast<void*>(ws), L.offsets),
+                                  at<int>(const_cast<void*>(ws), L.perm), at<int>(const_cast<void*>(ws), L.inv),
+                                  at<int>(const_cast<void*>(ws), L.tiles), at<int>(const_cast<void*>(ws), L.ntiles),
+                                  max_tiles(T * cfg->topk, cfg->n_experts, kGemmBM), bm, flags, stream));
+  return MOE_OK;
+}
+
 moe_status moe_debug_ws_offset(const moe_config* cfg, int32_t max_tokens, int32_t region, size_t* offset) {
   if (!offset || max_tokens < 0) return MOE_EINVAL;
   moe_status st = check_cfg(cfg);

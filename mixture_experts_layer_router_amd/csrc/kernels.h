@@ -62,6 +62,8 @@ hipError_t launch_permute(const int* ids, int TK, int E, int* hist, int* offsets
 // (fine <= 1024; row i counts slots [i*fine, (i+1)*fine)).
 hipError_t launch_permute_scatter(const int* ids, int TK, int E, const int* hist, int fine, int* offsets,
                                   int* perm_src, int* inv_pos, int* tiles, int* ntiles, int bm, hipStream_t s);
+hipError_t launch_validate_dispatch(const int* ids, int TK, int E, const int* offsets, const int* perm, const int* inv,
+                                   const int* tiles, const int* ntiles, int maxt, int bm, int* flags, hipStream_t s);
 hipError_t launch_build_tiles(const int* offsets, int E, int rows, int bm, int* tiles, int* ntiles, hipStream_t s);
 inline int max_tiles(int rows, int E, int bm) { return (rows + bm - 1) / bm + E; }
 // Row offset step of one expert's grouped-GEMM tiles: an expert with cnt rows

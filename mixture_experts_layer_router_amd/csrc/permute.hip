@@ -214,6 +214,69 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int* __restrict_
   write_tiles(cnt, E, bm, tiles, ntiles, scratch);
 }
 
+// Debug check of a dispatch (one workgroup, reads only, never traps): ORs
+// into *flags bit 0 if offsets[0] != 0 or offsets decrease, bit 1 if
+// offsets[E] != TK, bit 2 for an id outside [0, E), bit 3 if perm_src is not
+// a bijection of [0, TK) with inv_pos its inverse, bit 4 if a position holds
+// a slot of another expert or a segment is not in ascending slot order, bit
+// 5 if the tile list does not cover each segment in order with ceil(cnt /
+// bm) tiles at the row step tile_step(cnt, bm).
+__global__ __launch_bounds__(256) void validate_dispatch_kernel(const int* __restrict__ ids, int TK, int E,
+                                                                const int* __restrict__ off,
+                                                                const int* __restrict__ perm,
+                                                                const int* __restrict__ inv,
+                                                                const int* __restrict__ tiles,
+                                                                const int* __restrict__ ntiles, int maxt, int bm,
+                                                                int* flags) {
+  __shared__ int s_bits, s_want;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bits = s_want = 0;
+  __syncthreads();
+  int bits = 0, want = 0;
+  for (int e = tid; e <= E; e += 256) {
+    if (e == 0 && off[0] != 0) bits |= 1;
+    if (e < E && off[e] > off[e + 1]) bits |= 1;
+    if (e == E && off[E] != TK) bits |= 2;
+    if (e < E) want += (max(off[e + 1] - off[e], 0) + bm - 1) / bm;
+  }
+  for (int i = tid; i < TK; i += 256) {
+    const int id = ids[i];
+    if (id < 0 || id >= E) bits |= 4;
+    const int p = perm[i];
+    if (p < 0 || p >= TK || inv[p] != i) {
+      bits |= 8;
+      continue;
+    }
+    int lo = 0, hi = E - 1;  // the segment holding position i: largest e with off[e] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    if (ids[p] != lo) bits |= 16;
+    if (i + 1 < off[lo + 1] && i + 1 < TK && perm[i + 1] <= p) bits |= 16;
+  }
+  const int n_raw = ntiles[0], n = min(max(n_raw, 0), maxt);  // the list holds at most maxt entries
+  if (tid == 0 && n != n_raw) bits |= 32;
+  for (int j = tid; j < n; j += 256) {
+    const int e = tiles[2 * j], m0 = tiles[2 * j + 1];
+    if (e < 0 || e >= E) {
+      bits |= 32;
+      continue;
+    }
+    const int cnt = off[e + 1] - off[e], step = tile_step(cnt, bm);
+    const bool first = j == 0 || tiles[2 * (j - 1)] != e;
+    if (m0 < 0 || m0 >= cnt || (first ? m0 != 0 : m0 != tiles[2 * (j - 1) + 1] + step)) bits |= 32;
+  }
+  if (bits) atomicOr(&s_bits, bits);
+  if (want) atomicAdd(&s_want, want);
+  __syncthreads();
+  if (tid == 0) {
+    if (s_want != n) s_bits |= 32;
+    if (s_bits) atomicOr(flags, s_bits);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int* ids, int TK, int E, int* hist, int* offsets, int* perm_src, int* inv_pos,
@@ -238,6 +301,13 @@ hipError_t launch_permute_scatter(const int* ids, int TK, int E, const int* hist
   const int nwg = (TK + per_wg - 1) / per_wg, nrows = (TK + fine - 1) / fine;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nwg), dim3(kChunk), 0, s, ids, TK, E, hist, nrows, fine, per_wg,
                      offsets, perm_src, inv_pos, tiles, ntiles, bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate_dispatch(const int* ids, int TK, int E, const int* offsets, const int* perm, const int* inv,
+                                   const int* tiles, const int* ntiles, int maxt, int bm, int* flags, hipStream_t s) {
+  hipLaunchKernelGGL(validate_dispatch_kernel, dim3(1), dim3(256), 0, s, ids, TK, E, offsets, perm, inv, tiles, ntiles,
+                     maxt, bm, flags);
   return hipGetLastError();
 }
 
