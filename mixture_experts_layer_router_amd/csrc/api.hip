@@ -261,8 +261,20 @@ moe_status do_route(const moe_config* c, const uint16_t* x, int T, const uint16_
   rf.rp = rp;
   rf.ids = ids;
   rf.w = w;
+  rf.slices = 1;
   LAUNCH("route_fused", launch_route_fused(rf, s));
   return MOE_OK;
+}
+
+// H slices of the batched router per block of kRouteBlock tokens: about one
+// workgroup per CU in all, at most 8, and at least 4 column blocks of 128 per
+// slice (half the workgroup's waves busy); 1 beyond the counters' capacity.
+// The partial logits fit the logits region: blocks x slices <= T for T > 8.
+int route_slices(int T, int H) {
+  const int blocks = (T + kRouteBlock - 1) / kRouteBlock;
+  if (blocks > kRouteCtrMax) return 1;
+  const int want = (256 + blocks - 1) / blocks;
+  return std::max(1, std::min({want, 8, (H / 128) / 4}));
 }
 
 // The batched routing stack: stage M (if any), router, top-k, the routed
@@ -289,6 +301,9 @@ moe_status route_dispatch(const moe_config* c, const uint16_t* h, int T, const N
   rf.xq = c->routed_afmt != A_NONE ? xq : nullptr;
   rf.xqs = xqs;
   rf.hist = at<int>(ws, L.rhist);
+  rf.slices = route_slices(T, c->hidden);
+  rf.part = at<float>(ws, L.logits);
+  rf.ctr = at<unsigned>(ws, L.counter + kRouteCtrOff);
   LAUNCH("route_fused", launch_route_fused(rf, s));
   LAUNCH("permute", launch_permute_scatter(ids, T * c->topk, c->n_experts, rf.hist, kRouteBlock * c->topk, off, perm,
                                            inv, tiles, ntiles, bm, s));

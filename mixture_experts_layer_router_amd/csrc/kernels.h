@@ -44,6 +44,13 @@ struct RouteFusedParams {
   void* xq;               // codes u8 [T][H] in afmt (FP8_1X128 / MXFP8_1X32), or null
   void* xqs;              // their scales
   int* hist;              // int32 [ceil(T/kRouteBlock)][E] slot counts per block, or null
+  // K split: each block of kRouteBlock tokens is routed by `slices` workgroups
+  // over contiguous ranges of H; they hand their partial logits over in
+  // `part` (fp32 [blocks][slices][kRouteBlock][E]) and the last one (per the
+  // counter of the block in `ctr`, zero between calls) adds them in slice order
+  int slices;             // 1: no split
+  float* part;
+  unsigned* ctr;
 };
 hipError_t launch_route_fused(const RouteFusedParams& p, hipStream_t s);
 // Stage M alone: x = bf16 RMSNorm(h) * gamma (the rounding of route_fused).
@@ -246,6 +253,10 @@ constexpr int kFusedCtrBytes = 49152;
 constexpr int kFusedErrorWord = 0;  // ctr[0] != 0: a bounded wait gave up (never expected)
 constexpr int kFusedEpochWord = 1;  // ctr[1]: launches so far modulo 0xffffffff, never reset
 constexpr int kFusedTagOff = 24576;  // bytes: tagged router logits, 64-bit [T][E]
+// bytes: the batched router's per-block counters (K split), after the tagged
+// logits; zero between calls (the last workgroup of a block resets its word)
+constexpr int kRouteCtrOff = 40960;
+constexpr int kRouteCtrMax = (kFusedCtrBytes - kRouteCtrOff) / 4;
 constexpr int kFusedXLdsMax = 65536;  // bytes of x (T * H bf16) the launch stages in LDS; above, x is read from L2
 hipError_t launch_fused_decode(const FusedDecodeParams& p, hipStream_t s);
 

@@ -28,6 +28,11 @@
 // Router rows are re-read by every workgroup (from L2): one workgroup per
 // 16 tokens keeps the rows each workgroup streams (router + its tokens' h)
 // small next to the per-CU load rate and fills the chip from 4,096 tokens.
+// Below that, each block of 16 tokens is split over `slices` workgroups along
+// H (contiguous ranges of 128-column blocks, each quantising its own
+// columns); they hand their partial logits over through memory, and the
+// workgroup that completes the block's counter adds them in slice order and
+// routes the block, so the result does not depend on which finishes last.
 #include "route_dev.h"
 
 namespace moe {
@@ -52,8 +57,10 @@ __global__ __launch_bounds__(kWv * 64) void route_fused_kernel(RouteFusedParams 
   __shared__ float sw[kTB * 16];
   __shared__ float sbias[EB * 16];
   __shared__ int scnt[EB * 16];
+  __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kTB;
+  const int S = p.slices, blk = blockIdx.x / S, z = blockIdx.x % S;  // token block, H slice
+  const int t0 = blk * kTB;
   const int T = p.T, H = p.H, E = p.rp.E, K = p.rp.K;
   for (int e = tid; e < EB * 16; e += kWv * 64) {
     sbias[e] = (p.bias && e < E) ? p.bias[e] : 0.f;
@@ -84,6 +91,7 @@ __global__ __launch_bounds__(kWv * 64) void route_fused_kernel(RouteFusedParams 
 #pragma unroll
   for (int j = 0; j < EB; ++j) wrow[j] = p.wr + size_t(min(16 * j + row, E - 1)) * H;  // B column = expert
   const int nb = H / 128;
+  const int blo = int(long(nb) * z / S), bhi = int(long(nb) * (z + 1) / S);  // this slice's column blocks
   // every load of a 128-column block (of half a block when there are many
   // expert blocks) is issued before any of its MFMAs, and with at most 2
   // expert blocks the next block's loads go out before this one's MFMAs too
@@ -183,19 +191,19 @@ __global__ __launch_bounds__(kWv * 64) void route_fused_kernel(RouteFusedParams 
   };
   if constexpr (EB <= 2) {  // two register sets: block b + kWv loads while block b computes
     Blk A, B;
-    int b = wave;
-    if (b < nb) load_blk(A, b, 0);
-    for (; b < nb; b += 2 * kWv) {
-      if (b + kWv < nb) load_blk(B, b + kWv, 0);
+    int b = blo + wave;
+    if (b < bhi) load_blk(A, b, 0);
+    for (; b < bhi; b += 2 * kWv) {
+      if (b + kWv < bhi) load_blk(B, b + kWv, 0);
       mfma_blk(A, b, 0);
       quant_blk(b);
-      if (b + kWv >= nb) break;
-      if (b + 2 * kWv < nb) load_blk(A, b + 2 * kWv, 0);
+      if (b + kWv >= bhi) break;
+      if (b + 2 * kWv < bhi) load_blk(A, b + 2 * kWv, 0);
       mfma_blk(B, b + kWv, 0);
       quant_blk(b + kWv);
     }
   } else {
-    for (int b = wave; b < nb; b += kWv) {
+    for (int b = blo + wave; b < bhi; b += kWv) {
       Blk A;
 #pragma unroll
       for (int s0 = 0; s0 < 4; s0 += NS) {
@@ -218,9 +226,35 @@ __global__ __launch_bounds__(kWv * 64) void route_fused_kernel(RouteFusedParams 
     float v = red(0, tl, e);
 #pragma unroll
     for (int w = 1; w < kWv; ++w) v += red(w, tl, e);
-    red(0, tl, e) = v + sbias[e];
+    red(0, tl, e) = S > 1 ? v : v + sbias[e];
   }
   __syncthreads();
+  if (S > 1) {
+    // hand the slice's partial logits over: agent-scope stores, complete
+    // before the block's counter is incremented; the workgroup that brings it
+    // to S adds the S parts in slice order (its own from LDS, the others with
+    // agent-scope loads) and routes the block
+    float* mine = p.part + (size_t(blk) * S + z) * kTB * E;
+    for (int i = tid; i < kTB * E; i += kWv * 64)
+      __hip_atomic_store(mine + i, red(0, i / E, i % E), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(p.ctr + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(S - 1);
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = tid; i < kTB * E; i += kWv * 64) {
+      const int tl = i / E, e = i % E;
+      float v = 0.f;
+      for (int zz = 0; zz < S; ++zz)
+        v += zz == z ? red(0, tl, e)
+                     : __hip_atomic_load(p.part + (size_t(blk) * S + zz) * kTB * E + i, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      red(0, tl, e) = v + sbias[e];
+    }
+    if (tid == 0) __hip_atomic_store(p.ctr + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
   // ---- top-k: wave w routes rows 2w, 2w+1
   const TopkLayout L(p.rp, lane);
 #pragma unroll 1
@@ -243,7 +277,7 @@ __global__ __launch_bounds__(kWv * 64) void route_fused_kernel(RouteFusedParams 
   }
   if (!p.hist) return;
   __syncthreads();
-  for (int e = tid; e < E; e += kWv * 64) p.hist[size_t(blockIdx.x) * E + e] = scnt[e];
+  for (int e = tid; e < E; e += kWv * 64) p.hist[size_t(blk) * E + e] = scnt[e];
 }
 
 // Stage M alone (the paths whose router does not stage x itself): one wave
@@ -261,7 +295,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* __res
 
 template <int EB>
 hipError_t launch_eb(const RouteFusedParams& p, hipStream_t s) {
-  const dim3 grid(unsigned((p.T + kTB - 1) / kTB));
+  const dim3 grid(unsigned((p.T + kTB - 1) / kTB * p.slices));
   const bool norm = p.gamma != nullptr;
   const int af = p.xq ? p.afmt : A_NONE;
 #define MOE_RF(NORM, AF) hipLaunchKernelGGL((route_fused_kernel<EB, NORM, AF>), grid, dim3(kWv * 64), 0, s, p)
@@ -290,7 +324,8 @@ hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* gamma, float e
 
 hipError_t launch_route_fused(const RouteFusedParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  if (p.H % 128 || p.rp.E > 256 || p.rp.K > 16) return hipErrorInvalidValue;
+  if (p.H % 128 || p.rp.E > 256 || p.rp.K > 16 || p.slices < 1) return hipErrorInvalidValue;
+  if (p.slices > 1 && (!p.part || !p.ctr || (p.T + kTB - 1) / kTB > kRouteCtrMax)) return hipErrorInvalidValue;
   switch ((p.rp.E + 15) / 16) {
     case 1: return launch_eb<1>(p, s);
     case 2: return launch_eb<2>(p, s);
