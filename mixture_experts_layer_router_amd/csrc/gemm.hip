@@ -61,7 +61,7 @@ constexpr int BKB = 128;     // bytes of K per step
 constexpr int kStages = 3;
 constexpr int kLdsA = BM * BKB;   // 16 KB
 constexpr int kLdsB = BNT * BKB;  // 32 KB
-constexpr int kMaxKSteps = kGemmMaxK / 128;
+static_assert(kGemmMaxK / 128 <= 64, "one 64-lane load holds a block's weight scales");
 
 template <int WF>
 MOE_DEV constexpr int scale_dmas() { return WF == W_MXFP8 ? 2 : (WF == W_FP8_B128 ? 1 : 0); }
@@ -74,8 +74,9 @@ MOE_DEV constexpr int dmas_per_stage() { return 4 + 8 + scale_dmas<WF>(); }
 struct Frag {
   i32x8 a[2][2];  // [32-row block i][K half]
   i32x8 b[4][2];  // [32-row B block j][K half]
-  uint32_t sa[2], sb[4];  // MXFP8: the four e8m0 scales of the step, one byte per K block
-  f32x4 fa[2][4];         // FP8_B128: activation scales of the lane's 16 rows per block i
+  uint32_t sa[2], sb[4];  // MXFP8: the four e8m0 scales of the step, one byte per K block;
+                          // FP8_B128: sa[i] holds the fp32 activation scale of the lane's row of block i
+  float w[2];             // FP8_B128: the step's weight scales of the wave's gate (or only) and up blocks
 };
 MOE_DEV void set_slot(i32x8& v, int c, i32x4 x) {
   if (c & 1)
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t sAS[kStages][BM];
   __shared__ __attribute__((aligned(16))) uint32_t sBS[WF == W_MXFP8 ? kStages : 1][WF == W_MXFP8 ? BNT : 1];
   __shared__ float sAmax[2][BM];
-  __shared__ float sWs[WF == W_FP8_B128 ? 4 : 1][2][WF == W_FP8_B128 ? kMaxKSteps : 1];
+  __shared__ __attribute__((aligned(16))) float sWs[WF == W_FP8_B128 ? 4 : 1][2][WF == W_FP8_B128 ? 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -160,23 +161,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   }
 #undef PHYS_ROW
   // FP8_B128 weight scales: one per (128 B rows, 128 K); a wave's B rows sit in
-  // one gate block and one up block (GATEUP) or one block.  All K steps' scales
-  // go to LDS before the main loop, which then issues no global load of its own.
+  // one gate block and one up block (GATEUP) or one block.  Each wave loads
+  // every K step's scales of its blocks (K/128 <= 64: one direct-to-LDS load
+  // per block, lane l fetching step l) ahead of the prologue's tile loads, so
+  // the prologue's wait covers them and the main loop issues no other load.
+  const uint8_t* ws_base[2] = {nullptr, nullptr};
+  uint32_t ows = 0;
   if constexpr (WF == W_FP8_B128) {
     const int kb = K / 128;
-    for (int q = tid; q < 4 * 2 * kb; q += 256) {
-      const int w = q / (2 * kb), gg = (q / kb) & 1, ks = q % kb;
-      const int wnq = w >> 1;
+    ows = uint32_t(min(lane, kb - 1)) * 4u;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
       const float* src;
       if (EPI == EPI_GATEUP)
         src = static_cast<const float*>(gg ? p.B1s : p.B0s) + size_t(e) * p.bs_stride + size_t(n0 / 128) * kb;
       else
         src = static_cast<const float*>(p.B0s) + size_t(e) * p.bs_stride +
-              size_t(min((n0 + 128 * wnq) / 128, N / 128 - 1)) * kb;
-      sWs[w][gg][ks] = src[ks];
+              size_t(min((n0 + 128 * wn) / 128, N / 128 - 1)) * kb;
+      ws_base[gg] = uniform_ptr(src);
     }
-    __syncthreads();
   }
+  auto wscale_dma = [&]() {
+    if constexpr (WF == W_FP8_B128) {
+      dma4(ows, ws_base[0], lds_addr(&sWs[wave][0][0]));
+      if constexpr (EPI == EPI_GATEUP) dma4(ows, ws_base[1], lds_addr(&sWs[wave][1][0]));
+    }
+  };
 
   const uint32_t lds_a0 = lds_addr(smem), lds_b0 = lds_a0 + kStages * kLdsA;
   // direct-to-LDS load d of K step kstep into stage st
@@ -257,87 +267,104 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
   // ------------------------------------------------------------ main loop
   const bool two = 64 * wm + 32 < mrows;  // this wave's second row block holds valid rows
-  // the down GEMMs' epilogues leave the pipelined form too few registers
-  constexpr bool B128_PIPE = EPI == EPI_GATEUP;
-  if constexpr (WF == W_FP8_B128 && B128_PIPE) {
-    // Pipelined like the other formats: the operands and activation scales
-    // of step s+1 are read among the MFMAs of step s, the loads of step s+3
-    // issued among them too.  One 128-byte step is one 128-deep scale block:
-    // per half jh of the B blocks, the first K half of every (i, j) block
-    // goes into a temporary, the second accumulates onto it, and the
-    // temporaries are promoted into acc with the activation scale of each
-    // row times the weight scale of the wave's B rows.
+  if constexpr (WF == W_FP8_B128) {
+    // One 128-byte step is one 128-deep scale block.  The matrix instruction
+    // takes the weight rows as its first operand, so a lane's 16 results of a
+    // block are 16 output columns of one row: the promotion scale of a block
+    // is one number per lane (the row's activation scale times the block's
+    // weight scale).  Blocks b = 2 NI h + 2 i + jj (B half h, row block i,
+    // j = 2 h + jj) go in pairs: both first-K-half MFMAs of a pair write a
+    // temporary t[b % 4], then both second halves accumulate onto it.  The
+    // promotion acc += t * scale is cut into chunks of 8 elements, chunk k of
+    // the step (block k/2) issued after MFMA k+3, the last three after the
+    // first MFMAs of the next step: between two MFMAs a wave issues in order,
+    // so at most one chunk of VALU work sits between them and the matrix pipe
+    // keeps busy.  A temporary is rewritten by the block four after its own,
+    // at least one MFMA after its last chunk.  The operands of step s+1 are
+    // read among the MFMAs of step s, the loads of step s+3 issued among them
+    // too.
     auto run = [&](auto ni_t) {
       constexpr int NI = decltype(ni_t)::value;
-      constexpr int NM = NI * 8;                // MFMAs per step: two per (i, j) block
-      constexpr int NR = NI * 4 + 16 + NI * 4;  // LDS reads: A slots, B slots, activation scale vectors
-      auto read_b128 = [&](int r, Frag& f, int st) {
-        if (r < NI * 4 + 16) {
-          read_op(r, f, st, ni_t);
-        } else {
-          const int v = r - NI * 4 - 16, i = v / 4, q = v % 4;
-          f.fa[i][q] = *reinterpret_cast<const f32x4*>(&sAS[st][64 * wm + 32 * i + 8 * q + 4 * g]);
-        }
+      constexpr int NBS = 4 * NI;               // blocks per step
+      constexpr int NM = 2 * NBS;               // MFMAs per step
+      constexpr int NR = NI * 4 + 16 + NI;      // LDS reads: A slots, B slots, activation scales
+      constexpr int kLag = 3;                   // chunk k follows MFMA k + kLag
+      f32x16 t[4];
+      float sc[NI][2];      // this step's promotion scales per (i, h)
+      float sc_last = 0.f;  // the previous step's scale of its last pair (i = NI-1, h = 1)
+      auto read_w = [&](Frag& f, int ks) {  // weight scales of K step ks (of this slice)
+        f.w[0] = sWs[wave][0][ks + ks0];
+        f.w[1] = sWs[wave][EPI == EPI_GATEUP ? 1 : 0][ks + ks0];
       };
-      auto step = [&](int s, Frag& cur, Frag& nxt) {
+      auto chunk = [&](int k, float scale) {
+        const int b = k / 2, c = k % 2;
+        const int h = b / (2 * NI), i = (b / 2) % NI, j = 2 * h + (b & 1);
+#pragma unroll
+        for (int r = 8 * c; r < 8 * c + 8; ++r) acc[i][j][r] = fmaf(t[b % 4][r], scale, acc[i][j][r]);
+      };
+      auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t) {
         wait_lgkm0();    // cur is in registers: this wave no longer reads stage s
         wait_vm<DPS>();  // this wave's loads of step s+1 have landed
         barrier();       // ... and every wave's; stage s % 3 is free for step s+3
         const int stn = (s + 1) % kStages, std_ = s % kStages;
         const int kd = min(s + 3, nk - 1) + ks0;
-        const float w0 = sWs[wave][0][s + ks0], w1 = sWs[wave][1][s + ks0];
-        f32x16 t[2][2];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          sc[i][0] = __uint_as_float(cur.sa[i]) * cur.w[0];
+          sc[i][1] = __uint_as_float(cur.sa[i]) * cur.w[1];
+        }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const int jh = m / (NI * 4), hf = (m / (NI * 2)) % 2, blk = m % (NI * 2);
-          const int i = blk / 2, jj = blk % 2, j = 2 * jh + jj;
-          {  // every B block (B rows past N are clamped loads; their columns are not stored)
-            if (hf == 0) {
-              f32x16 z;
+          const int p4 = m / 4, q = m % 2, kq = (m / 2) % 2;
+          const int b = 2 * p4 + q;
+          const int h = b / (2 * NI), i = (b / 2) % NI, j = 2 * h + (b & 1);
+          if (kq == 0) {
+            f32x16 z;
 #pragma unroll
-              for (int r = 0; r < 16; ++r) z[r] = 0.f;
-              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i][0], cur.b[j][0], z, 0, 0, 0, 127, 0,
-                                                                         127);
-            } else {
-              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i][1], cur.b[j][1], t[i][jj], 0, 0, 0,
-                                                                         127, 0, 127);
-            }
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            t[b % 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j][0], cur.a[i][0], z, 0, 0, 0, 127, 0, 127);
+          } else {
+            t[b % 4] =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j][1], cur.a[i][1], t[b % 4], 0, 0, 0, 127, 0, 127);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int r = (m * NR) / NM; r < ((m + 1) * NR) / NM; ++r) read_b128(r, nxt, stn);
+          for (int r = (m * NR) / NM; r < ((m + 1) * NR) / NM; ++r) read_op(r, nxt, stn, ni_t);
+          if (m == NM / 2) read_w(nxt, min(s + 1, nk - 1));
 #pragma unroll
           for (int d = (m * DPS) / NM; d < ((m + 1) * DPS) / NM; ++d) dma_op(d, std_, kd);
           __builtin_amdgcn_sched_barrier(0);
-          if (hf == 1 && blk == NI * 2 - 1) {  // the half's temporaries are complete: promote them
-            const float wj = (EPI == EPI_GATEUP && jh == 1) ? w1 : w0;
-#pragma unroll
-            for (int ii = 0; ii < NI; ++ii)
-#pragma unroll
-              for (int j2 = 0; j2 < 2; ++j2) {
-                const int jo = 2 * jh + j2;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                  acc[ii][jo][r] = fmaf(t[ii][j2][r], cur.fa[ii][r / 4][r % 4] * wj, acc[ii][jo][r]);
-              }
+          if (m >= kLag) {
+            const int k = m - kLag, bk = k / 2;
+            chunk(k, sc[(bk / 2) % NI][bk / (2 * NI)]);
+          } else if constexpr (!decltype(first_t)::value) {
+            chunk(m - kLag + NM, sc_last);  // the previous step's last pair
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
+        sc_last = sc[NI - 1][1];
       };
       Frag f0, f1;
+      wscale_dma();
       issue(0);
       issue(min(1, nk - 1));
       issue(min(2, nk - 1));
-      wait_vm<2 * DPS>();
+      wait_vm<2 * DPS>();  // the weight scales and step 0
       barrier();
 #pragma unroll
-      for (int r = 0; r < NR; ++r) read_b128(r, f0, 0);
-      step(0, f0, f1);
+      for (int r = 0; r < NR; ++r) read_op(r, f0, 0, ni_t);
+      read_w(f0, 0);
+      const std::true_type first{};
+      const std::false_type later{};
+      step(0, f0, f1, first);
       int s = 1;
       for (; s + 1 < nk; s += 2) {
-        step(s, f1, f0);
-        step(s + 1, f0, f1);
+        step(s, f1, f0, later);
+        step(s + 1, f0, f1, later);
       }
-      if (s < nk) step(s, f1, f0);
+      if (s < nk) step(s, f1, f0, later);
+#pragma unroll
+      for (int k = NM - kLag; k < NM; ++k) chunk(k, sc_last);  // the last step's pending chunks
     };
     if (nk > 0) {
       if (two)
@@ -345,69 +372,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
       else
         run(IC<1>{});
     }
-  } else if constexpr (WF == W_FP8_B128) {
-    // the down GEMMs: the pipelined form's registers do not fit beside their
-    // epilogue, so each step reads its operands when it starts
-    auto run = [&](auto ni_t) {
-      constexpr int NI = decltype(ni_t)::value;
-      if (nk > 0) issue(0);
-      if (nk > 1) issue(1);
-      for (int s = 0; s < nk; ++s) {
-        const int st = s % kStages;
-        if (s + 1 < nk)
-          wait_vm<DPS>();
-        else
-          wait_vm<0>();
-        barrier();
-        if (s + 2 < nk) issue(s + 2);
-        Frag f;
-#pragma unroll
-        for (int r = 0; r < NI * 4 + 16; ++r) read_op(r, f, st, ni_t);
-        // activation scales of the lane's 16 output rows per block: rows 8q + 4g + [0, 4)
-        f32x4 fa[2][4];
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            fa[i][q] = *reinterpret_cast<const f32x4*>(&sAS[st][64 * wm + 32 * i + 8 * q + 4 * g]);
-        const float w0 = sWs[wave][0][s + ks0], w1 = sWs[wave][1][s + ks0];
-#pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          f32x16 t[2][2];
-#pragma unroll
-          for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int j = 2 * jh + jj;
-              f32x16 z;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) z[r] = 0.f;
-              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i][0], f.b[j][0], z, 0, 0, 0, 127, 0,
-                                                                         127);
-            }
-#pragma unroll
-          for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int j = 2 * jh + jj;
-              t[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i][1], f.b[j][1], t[i][jj], 0, 0, 0,
-                                                                         127, 0, 127);
-            }
-          const float wj = (EPI == EPI_GATEUP && jh == 1) ? w1 : w0;
-#pragma unroll
-          for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                acc[i][2 * jh + jj][r] = fmaf(t[i][jj][r], fa[i][r / 4][r % 4] * wj, acc[i][2 * jh + jj][r]);
-        }
-      }
-    };
-    if (two)
-      run(IC<2>{});
-    else
-      run(IC<1>{});
   } else {
     auto run = [&](auto ni_t) {
       constexpr int NI = decltype(ni_t)::value;
@@ -478,9 +442,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < 2; ++jj) {
+        if constexpr (WF == W_FP8_B128) {  // lane: row 64 wm + 32 i + l%32, columns 8 q + 4 (l/32) + [0, 4)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) hb[row_of(i, r) * RSF + 64 * wn + 32 * jj + l32] = acc[i][jj][r];
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(hb + (64 * wm + 32 * i + l32) * RSF + 64 * wn + 32 * jj + 8 * q + 4 * g) =
+                f32x4{acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) hb[row_of(i, r) * RSF + 64 * wn + 32 * jj + l32] = acc[i][jj][r];
+        }
+      }
     __syncthreads();
     const int row = tid & 127, half = tid >> 7;  // this thread: h columns n0 + 64 half + [0, 64) of tile row `row`
     f32x4 v[16];
@@ -553,6 +525,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
           if (half == 0) static_cast<float*>(p.Cs)[orow * (N / 128) + n0 / 128] = sc;
         }
       }
+    }
+  } else if constexpr (WF == W_FP8_B128) {
+    // lane: row 64 wm + 32 i + l%32, columns 32 j + 8 q + 4 (l/32) + [0, 4) of the wave's 128
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rl = 64 * wm + 32 * i + l32;
+      if (rl >= mrows) continue;
+      const size_t orow = size_t(seg0 + m0 + rl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + 128 * wn + 32 * j + 8 * q + 4 * g;
+          if (col >= N) continue;
+          const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (EPI == EPI_F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.C) + kz * p.c_split + orow * p.ldc + col) = v;
+          } else {
+            const uint32_t lo = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + orow * p.ldc + col) = uint2{lo, hi};
+          }
+        }
     }
   } else {
 #pragma unroll
