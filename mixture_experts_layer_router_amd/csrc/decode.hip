@@ -14,10 +14,15 @@
 // last router row, where counting the rows and raising a flag would cost
 // three (two atomics and the flag read) on a memory system busy with weight
 // streams.  The rest of the work is a list of items in dependency order:
-//   SU  shared gate/up         (8 intermediate columns of one token)
-//   RG  routed gate/up         (8 intermediate columns of one (token, slot))
+//   SU  shared gate/up         (8 intermediate columns of every token from 3
+//                               tokens on, else of one token)
+//   RG  routed gate/up         (8 intermediate columns of one distinct expert
+//                               for every slot that chose it from 3 tokens
+//                               on, else of one (token, slot))
 //   DN  down + combine         (4 output rows of one token: the shared and
 //                               the K routed down matrices as one long dot)
+// From 3 tokens on a gate/up weight row is thus read once per launch, not
+// once per token or slot (8 tokens: 256 -> 233 us per layer).
 // RG needs all router rows (each workgroup runs the top-k itself from the
 // logits); DN needs the routing for its weight addresses and SU + RG for h.
 // A DN item issues its weight loads first and only then waits for h, so the
@@ -58,9 +63,6 @@ namespace {
 constexpr int kQ = 32;         // queues, and most stripes of a counter
 constexpr int kLine = 32;      // words per 128-byte line
 constexpr int kUR = 2;         // intermediate columns per wave in a gate/up item
-constexpr int kUC = 1;         // weight chunks (1 KB) per row loaded together: one per round, so a
-                               // wave's requests are spread over its item (streams better than all
-                               // of an item's loads at once: 48.0 against 50.3 us per layer)
 constexpr int kUpCols = 4 * kUR;
 constexpr int kSUR = 2;        // ... in a shared gate/up item
 constexpr int kSUpCols = 4 * kSUR;
@@ -252,24 +254,29 @@ MOE_DEV const MOE_GLOBAL uint8_t* uni(const void* p) {
 }
 
 
-// h[i0 .. i0+NR) = SiLU(x.Wg^T) * (x.Wu^T) for the token whose bf16 x row sits
-// in LDS as packed pairs (xl).  NC weight chunks of each of the 2 NR rows are
-// loaded together, then reduced, then the next NC; x comes from LDS, so the
-// registers hold only weights and scales.  h
-// is stored with agent-scope atomic stores (read by other workgroups inside
-// the launch once the phase is published).  pre() runs once every load has
-// been consumed and before the store.
 // 16 bytes of x as bf16 pairs, from LDS or (x in global memory) with a global load
 MOE_DEV u32x4 ldx4(const uint32_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 MOE_DEV u32x4 ldx4(const MOE_GLOBAL uint32_t* p) { return *reinterpret_cast<const MOE_GLOBAL u32x4*>(p); }
 
-template <int WF, int NR, int NC, class XP, class Pre>
-MOE_DEV void gate_up_lds(XP xl, int H, const void* g, const void* u, const void* gs, const void* us,
-                         int i0, float* hrow, Pre pre) {
+// h[j][i0 .. i0+NR) = SiLU(x_j.Wg^T) * (x_j.Wu^T) for nt <= MAXT token rows
+// (bf16 pairs; x row j at xrow(j), in LDS or global memory; h row j at
+// hrow(j)).  Each weight chunk is read once, turned into bf16 pairs once
+// (the same pairs and sum order as dot_chunk_bx) and dotted with the x of
+// every token, so a matrix row that several tokens need streams from HBM
+// once.  One 1 KB chunk per row is in flight per round, so a wave's requests
+// spread over its item (that streams better than all of an item's loads at
+// once: 48.0 against 50.3 us per B=1 layer).  h is stored with agent-scope
+// atomic stores (read by other workgroups inside the launch once the phase
+// is published), lane NR * j + r storing h[j][i0 + r]; pre() runs once
+// every load has been consumed and before the store.
+constexpr int kXG = 4;  // tokens whose x chunk a gate/up wave holds at once
+template <int WF, int NR, int MAXT, class XRow, class HRow, class Pre>
+MOE_DEV void gate_up_multi(XRow xrow, int nt, int H, const void* g, const void* u, const void* gs, const void* us,
+                           int i0, HRow hrow, Pre pre) {
   constexpr int CW = Fmt<WF>::CW, EPL = Fmt<WF>::EPL, ES = Fmt<WF>::ES;
   constexpr int NS = WF == W_MXFP8 ? NR : 1;  // scales per chunk (FP8_B128: the rows share a 128-row block)
+  static_assert(NR * MAXT <= 64, "one lane per stored h value");
   const int lane = lane_id();
-  // row bases are uniform (scalar registers); each lane adds a 32-bit offset
   const MOE_GLOBAL uint8_t* gb[NR];
   const MOE_GLOBAL uint8_t* ub[NR];
 #pragma unroll
@@ -279,66 +286,88 @@ MOE_DEV void gate_up_lds(XP xl, int H, const void* g, const void* u, const void*
   }
   const MOE_GLOBAL uint8_t* gsb = nullptr;
   const MOE_GLOBAL uint8_t* usb = nullptr;
-  if (WF == W_FP8_B128) {  // the 128-row block's scale row
+  if (WF == W_FP8_B128) {
     gsb = uni(static_cast<const uint8_t*>(gs) + size_t(i0 >> 7) * (H >> 7) * 4);
     usb = uni(static_cast<const uint8_t*>(us) + size_t(i0 >> 7) * (H >> 7) * 4);
   }
-  float ag[NR] = {}, au[NR] = {};
+  float ag[NR][MAXT], au[NR][MAXT];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) ag[r][j] = au[r][j] = 0.f;
   const int kl = lane * EPL;
-  for (int k0 = 0; k0 < H; k0 += NC * CW) {
-    u32x4 wg[NC][NR], wu[NC][NR];
-    float sg[NC][NS], su[NC][NS];
+  for (int k0 = 0; k0 < H; k0 += CW) {
+    const bool valid = k0 + kl < H;  // lanes past the row end add 0
+    const uint32_t k = uint32_t(min(k0 + kl, H - EPL));
+    u32x4 wg[NR], wu[NR];
+    float sg[NS], su[NS];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c > 0 && k0 + c * CW >= H) break;  // uniform
-      const uint32_t k = uint32_t(min(k0 + c * CW + kl, H - EPL));
+    for (int r = 0; r < NR; ++r) {
+      wg[r] = *reinterpret_cast<const MOE_GLOBAL u32x4*>(gb[r] + k * ES);
+      wu[r] = *reinterpret_cast<const MOE_GLOBAL u32x4*>(ub[r] + k * ES);
+    }
+    if (WF == W_FP8_B128) {
+      sg[0] = *reinterpret_cast<const MOE_GLOBAL float*>(gsb + (k >> 7) * 4);
+      su[0] = *reinterpret_cast<const MOE_GLOBAL float*>(usb + (k >> 7) * 4);
+    } else {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        wg[c][r] = *reinterpret_cast<const MOE_GLOBAL u32x4*>(gb[r] + k * ES);
-        wu[c][r] = *reinterpret_cast<const MOE_GLOBAL u32x4*>(ub[r] + k * ES);
-      }
-      if (WF == W_FP8_B128) {
-        sg[c][0] = *reinterpret_cast<const MOE_GLOBAL float*>(gsb + (k >> 7) * 4);
-        su[c][0] = *reinterpret_cast<const MOE_GLOBAL float*>(usb + (k >> 7) * 4);
-      } else {
-#pragma unroll
-        for (int r = 0; r < NS; ++r) {
-          sg[c][r] = wscale<WF>(gs, i0 + r, int(k), H);
-          su[c][r] = wscale<WF>(us, i0 + r, int(k), H);
-        }
+      for (int r = 0; r < NS; ++r) {
+        sg[r] = wscale<WF>(gs, i0 + r, int(k), H);
+        su[r] = wscale<WF>(us, i0 + r, int(k), H);
       }
     }
+    uint32_t pg[NR][EPL / 2], pu[NR][EPL / 2];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c > 0 && k0 + c * CW >= H) break;
-      const int kr = k0 + c * CW + kl;
-      const bool valid = kr < H;  // lanes past the row end add 0
-      const int k = min(kr, H - EPL);
-      uint32_t xp[EPL / 2];
+    for (int r = 0; r < NR; ++r) {
+      bf16_pairs<WF>(wg[r], pg[r]);
+      bf16_pairs<WF>(wu[r], pu[r]);
+    }
+    // x of at most kXG tokens in registers at once
 #pragma unroll
-      for (int i = 0; i < EPL / 8; ++i) {
-        const u32x4 v = ldx4(xl + k / 2 + 4 * i);
+    for (int j0 = 0; j0 < MAXT; j0 += kXG) {
+      if (j0 >= nt) break;  // uniform
+      uint32_t xp[kXG][EPL / 2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xp[4 * i + q] = v[q];
+      for (int jj = 0; jj < kXG; ++jj) {
+        if (j0 + jj >= nt || j0 + jj >= MAXT) break;
+        const auto xr = xrow(j0 + jj);
+#pragma unroll
+        for (int i = 0; i < EPL / 8; ++i) {
+          const u32x4 v = ldx4(xr + k / 2 + 4 * i);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xp[jj][4 * i + q] = v[q];
+        }
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const float sgr = valid ? sg[c][NS > 1 ? r : 0] : 0.0f;
-        const float sur = valid ? su[c][NS > 1 ? r : 0] : 0.0f;
-        ag[r] = fmaf(dot_chunk_bx<WF>(wg[c][r], xp), sgr, ag[r]);
-        au[r] = fmaf(dot_chunk_bx<WF>(wu[c][r], xp), sur, au[r]);
+        const float sgr = valid ? sg[NS > 1 ? r : 0] : 0.0f;
+        const float sur = valid ? su[NS > 1 ? r : 0] : 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < kXG; ++jj) {
+          const int j = j0 + jj;
+          if (j >= nt || j >= MAXT) break;
+          ag[r][j] = fmaf(dot_pairs<EPL / 2>(pg[r], xp[jj]), sgr, ag[r][j]);
+          au[r][j] = fmaf(dot_pairs<EPL / 2>(pu[r], xp[jj]), sur, au[r][j]);
+        }
       }
     }
   }
   float mine = 0.f;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float gv = wave_sum(ag[r]);
-    const float uv = wave_sum(au[r]);
-    if (lane == r) mine = silu(gv) * uv;
+  for (int j = 0; j < MAXT; ++j) {
+    if (j >= nt) break;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float gv = wave_sum(ag[r][j]);
+      const float uv = wave_sum(au[r][j]);
+      if (lane == NR * j + r) mine = silu(gv) * uv;
+    }
   }
   pre();
-  if (lane < NR) __hip_atomic_store(hrow + i0 + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane < NR * nt) {
+    const int j = lane / NR, r = lane % NR;
+    __hip_atomic_store(hrow(j) + i0 + r, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // XG: x is read from global memory (L2) instead of being staged in LDS, for
@@ -352,13 +381,23 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   __shared__ float dpart[4][kDR];
   __shared__ int sids[MAXT * 16];
   __shared__ float sw[MAXT * 16];
+  // the distinct routed experts of the launch in ascending id order, and per
+  // distinct expert u its slots (token-major order) and their number
+  __shared__ int s_uexp[MAXT * 16], s_unt[MAXT * 16], s_uslot[MAXT * 16][MAXT];
+  __shared__ unsigned s_bits[8];
+  __shared__ int s_nuniq;
   __shared__ unsigned s_next;
   __shared__ int s_ok, s_last, s_rok;
   const DecodeParams& d = p.d;
   const Ctr c{p.ctr};
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = d.T, H = d.H, K = d.rp.K, E = d.rp.E, I = p.I, Is = d.Is;
-  const int n[4] = {E, Is ? T * (Is / kSUpCols) : 0, T * K * (I / kUpCols), T * (H / kDR)};
+  // from 3 tokens on, a shared gate/up item serves every token and a routed
+  // one every slot of one distinct expert (each weight row read once); at 1
+  // and 2 tokens the second reads come from the caches and the items stay
+  // per token and per slot (measured: 2 tokens 81 against 84 us)
+  const bool dedup = T > 2;
+  const int n[4] = {E, Is ? (dedup ? 1 : T) * (Is / kSUpCols) : 0, T * K * (I / kUpCols), T * (H / kDR)};
   const int b1 = 0, b2 = b1 + n[1], b3 = b2 + n[2];  // queue items: SU, RG, DN (R is static)
   const unsigned total = unsigned(b3 + n[3]);
   const int q = blockIdx.x % kQ;
@@ -416,11 +455,11 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
       if (tid == 0) s_next = q + kQ * next;
     };
     const int it = int(item);
-    if (it < b2) {  // SU: 8 shared intermediate columns of one token
+    if (it < b2) {  // SU: 8 shared intermediate columns of every token (dedup), else of one token
       const int i = it - b1, per = Is / kSUpCols;
-      const int t = i / per, c0 = (i % per) * kSUpCols + wave * kSUR;
-      gate_up_lds<WF, kSUR, kUC>(xrow(t), H, d.sg, d.su, d.sgs, d.sus, c0, d.hs + size_t(t) * Is,
-                                 hand_over);
+      const int t0 = dedup ? 0 : i / per, c0 = (dedup ? i : i % per) * kSUpCols + wave * kSUR;
+      gate_up_multi<WF, kSUR, MAXT>([&](int j) { return xrow(t0 + j); }, dedup ? T : 1, H, d.sg, d.su, d.sgs, d.sus,
+                                    c0, [&](int j) { return d.hs + size_t(t0 + j) * Is; }, hand_over);
     } else {
       if (!have_topk) {  // every workgroup routes all T tokens itself (wave w: tokens w, w + 4)
         for (int tt = wave; tt < T; tt += 4) {
@@ -430,26 +469,69 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
             s_rok = 0;
           topk_select(d.rp, L, lg, sids + tt * K, sw + tt * K);
         }
+        __syncthreads();  // every token's ids are in LDS
+        // the distinct experts (ids clamped into [0, E) as every consumer
+        // of an id does) and the slots that chose each
+        if (MAXT == 1 || !dedup) {  // one routed item per slot
+          if (tid < T * K) {
+            s_uexp[tid] = min(max(sids[tid], 0), E - 1);
+            s_unt[tid] = 1;
+            s_uslot[tid][0] = tid;
+          }
+          if (tid == 0) s_nuniq = T * K;
+        } else {
+          if (tid < 8) s_bits[tid] = 0u;
+          __syncthreads();  // s_bits is zero
+          const int TK = T * K;
+          const int e_mine = tid < TK ? min(max(sids[tid], 0), E - 1) : 0;
+          if (tid < TK) atomicOr(&s_bits[e_mine >> 5], 1u << (e_mine & 31));
+          __syncthreads();
+          if (tid < TK) {
+            int u = __popc(s_bits[e_mine >> 5] & ((1u << (e_mine & 31)) - 1u));
+            for (int w = 0; w < (e_mine >> 5); ++w) u += __popc(s_bits[w]);
+            int j = 0, cnt = 0;
+            for (int s2 = 0; s2 < TK; ++s2) {
+              const bool same = min(max(sids[s2], 0), E - 1) == e_mine;
+              j += same && s2 < tid;
+              cnt += same;
+            }
+            s_uslot[u][j] = tid;
+            if (j == 0) {
+              s_uexp[u] = e_mine;
+              s_unt[u] = cnt;
+            }
+          }
+          if (tid == 0) {
+            int nu = 0;
+            for (int w = 0; w < 8; ++w) nu += __popc(s_bits[w]);
+            s_nuniq = nu;
+          }
+        }
         __syncthreads();
         poisoned |= s_rok == 0;
         have_topk = true;
       }
-      if (it < b3) {  // RG: 8 routed intermediate columns of one (token, slot)
+      if (it < b3) {  // RG: 8 routed intermediate columns of one distinct expert for every slot that chose
+                      // it (dedup), else of one slot
         const int i = it - b2;
         if (i == 0 && tid < T * K) {  // one workgroup publishes the routing
           store_agent(d.ids + tid, sids[tid]);
           store_agent(d.w + tid, sw[tid]);
         }
         const int per = I / kUpCols;
-        const int slot = i / per, c0 = (i % per) * kUpCols + wave * kUR;
-        const int e = min(max(sids[slot], 0), E - 1);
-        const size_t ws = wstride<WF>(I, H), ss = sstride<WF>(I, H);
-        const uint8_t* ge = static_cast<const uint8_t*>(p.g) + e * ws;
-        const uint8_t* ue = static_cast<const uint8_t*>(p.u) + e * ws;
-        const uint8_t* gse = p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr;
-        const uint8_t* use = p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr;
-        gate_up_lds<WF, kUR, kUC>(xrow(slot / K), H, ge, ue, gse, use, c0, p.h + size_t(slot) * I,
-                                  hand_over);
+        const int u = i / per, c0 = (i % per) * kUpCols + wave * kUR;
+        if (u < s_nuniq) {  // items past the distinct experts (T * K of them at most) have no work
+          const int e = s_uexp[u];
+          const size_t ws = wstride<WF>(I, H), ss = sstride<WF>(I, H);
+          const uint8_t* ge = static_cast<const uint8_t*>(p.g) + e * ws;
+          const uint8_t* ue = static_cast<const uint8_t*>(p.u) + e * ws;
+          const uint8_t* gse = p.gs ? static_cast<const uint8_t*>(p.gs) + e * ss : nullptr;
+          const uint8_t* use = p.us ? static_cast<const uint8_t*>(p.us) + e * ss : nullptr;
+          gate_up_multi<WF, kUR, MAXT>([&](int j) { return xrow(s_uslot[u][j] / K); }, s_unt[u], H, ge, ue, gse, use,
+                                       c0, [&](int j) { return p.h + size_t(s_uslot[u][j]) * I; }, hand_over);
+        } else {
+          hand_over();
+        }
       } else {  // DN: kDR output rows of one token over [shared Is | routed K*I]
         const int i = it - b3, nb = H / kDR;
         const int t = i / nb, n0 = (i % nb) * kDR;
@@ -571,6 +653,7 @@ hipError_t launch_fused(const FusedDecodeParams& p, hipStream_t s) {
 template <int WF>
 hipError_t launch_fused_x(const FusedDecodeParams& p, hipStream_t s) {
   if (size_t(p.d.T) * p.d.H * 2 > size_t(kFusedXLdsMax)) return launch_fused<WF, true, kRouteGemvMaxT>(p, s);
+  if (p.d.T == 1) return launch_fused<WF, false, 1>(p, s);
   if (p.d.T <= 4) return launch_fused<WF, false, 4>(p, s);
   return launch_fused<WF, false, kRouteGemvMaxT>(p, s);
 }

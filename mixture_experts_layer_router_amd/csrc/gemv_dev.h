@@ -76,6 +76,34 @@ MOE_DEV float dot_chunk_bx(u32x4 w, const uint32_t* xp) {
   return s0 + s1;
 }
 
+// one 16-byte weight chunk as EPL/2 bf16 pairs, in dot_chunk_bx's order
+template <int WF>
+MOE_DEV void bf16_pairs(u32x4 w, uint32_t (&p)[Fmt<WF>::EPL / 2]) {
+  const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
+  if (WF == W_BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = wq[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      p[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wq[q], 1.0f, false));
+      p[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wq[q], 1.0f, true));
+    }
+  }
+}
+// dot of NP weight pairs with NP activation pairs: even pairs into one sum,
+// odd pairs into the other, as dot_chunk_bx
+template <int NP>
+MOE_DEV float dot_pairs(const uint32_t (&w)[NP], const uint32_t* xp) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < NP; q += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[q]), as_bf16x2(xp[q]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[q + 1]), as_bf16x2(xp[q + 1]), s1, false);
+  }
+  return s0 + s1;
+}
+
 // scale of weight element (row n, column k) of an [N][L] matrix
 template <int WF>
 MOE_DEV float wscale(const void* S, int n, int k, int L) {
