@@ -412,6 +412,37 @@ def test_forward_b128_bf16x_small_t(T, path, monkeypatch):
     assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
 
 
+@pytest.mark.parametrize("T,hidden,forced", [(3, 640, 5), (5, 640, 3), (8, 640, 5), (8, 4608, 5), (8, 4608, 3)])
+def test_single_launch_repeated_experts(T, hidden, forced):
+    """From 3 tokens on, the single launch runs one routed gate/up item per
+    distinct expert, for every slot that chose it.  A bias every token
+    follows puts `forced` of the 5 slots on the same experts for all tokens
+    (the other slots free), so a distinct expert serves up to T slots; at
+    hidden 4608 the 8 tokens' x is read from global memory instead of LDS.
+    Ids, weights and output match the oracle; a second call is bitwise equal."""
+    cfg = small_cfg(1, tokens=T, hidden=hidden, n_experts=24, n_groups=4, topk_groups=2, topk=5, inter=384,
+                    shared_inter=512)
+    inp = synth.make_inputs(cfg, DEV)
+    bias = torch.zeros(cfg.n_experts, device=DEV)
+    chosen = [0, 1, 2, 6, 7][:forced]  # in groups 0 and 1 (6 experts per group)
+    bias[chosen] = 30.0
+    inp.bias = bias
+    inp = ensure_margin(inp)
+    say(f"[repeated experts] T={T} H={hidden} forced={forced}")
+    layer = moe.Layer(cfg, inp)
+    out, ids, w = _forward(cfg, inp, layer=layer)
+    moe.workspace_check(layer.ws)
+    ids_np = ids.cpu().numpy()
+    for e in chosen:
+        assert (ids_np == e).any(axis=1).all()  # every token holds every forced expert
+    r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
+    assert np.array_equal(ids_np, r.ids)
+    assert np.max(np.abs(w.cpu().numpy() - r.w) / r.w) <= WTOL
+    assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
+    out2, _, _ = _forward(cfg, inp, layer=layer)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
 @pytest.mark.parametrize("name,path", [("dsv2_like_4tok", "auto"), ("dsv2_like_4tok", "staged"),
                                        ("b128_12exp_97tok", "auto"), ("zipf_16exp_200tok", "auto"),
                                        ("tiny_8tok", "auto"), ("mx_4exp_160tok", "auto")])
