@@ -328,6 +328,7 @@ def batched(moe, synth, torch, steps=20, names=("dsv2_256tok", "dsv2_4096tok_zip
         inp = synth.make_inputs(cfg, "cuda:0")
         lay = moe.Layer(cfg, inp)
         ms, _ = time_layers([lay], [inp.x], steps, 3, torch)
+        stats = block_stats([lay], [inp.x], 10, 2, torch)
         _, ids, _ = lay.forward()
         torch.cuda.synchronize()
         touched = sorted(set(ids.flatten().tolist()))
@@ -337,7 +338,7 @@ def batched(moe, synth, torch, steps=20, names=("dsv2_256tok", "dsv2_4096tok_zip
         flops = 2.0 * T * K * 3 * H * I + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
         kern = trace_kernels([lay], [inp.x], 3, moe, torch)
         cnt = np.bincount(ids.flatten().cpu().numpy(), minlength=E)
-        res.append({"workload": name, "tokens": T, "us_per_layer": round(ms * 1e3, 2),
+        res.append({"workload": name, "tokens": T, "us_per_layer": round(ms * 1e3, 2), "step_us_stats": stats,
                     "max_mean_load": round(float(cnt.max() / cnt.mean()), 2), "empty_experts": int((cnt == 0).sum()),
                     "roofline": gemm_roofline(name, kern, T * K, H, I, "gemm_gate_up_routed"),
                     "touched_experts": len(touched), "algorithmic_bytes": int(nbytes),
