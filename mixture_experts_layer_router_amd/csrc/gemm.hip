@@ -584,6 +584,8 @@ hipError_t launch_epi(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, hipStream_t s) {
+  // FP8_B128: every K step's weight scales sit in one 64-entry LDS row per block
+  if (wfmt == W_FP8_B128 && (p.K > kGemmMaxK || p.K % 128)) return hipErrorInvalidValue;
   if (gemm2_chosen(wfmt, epi, p)) return launch_gemm2(wfmt, epi, p, s);
   const int ntile = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
   if (ntile <= 0) return hipSuccess;
