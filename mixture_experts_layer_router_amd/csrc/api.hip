@@ -370,7 +370,7 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
 
 // The batched shared FFN on all T rows of x, on stream s, using only its own
 // workspace regions (x quantised into xs2 in the shared activation format,
-// h in hsh, y in ysh); *ysh gets the fp32 output rows.
+// h in hsh, y in ysh); *ysh gets the output rows, bf16 like Y_perm.
 moe_status shared_ffn(const moe_config* cfg, const uint16_t* x, int T, const moe_ffn_weights* shared, void* ws,
                       const Ws& L, float** ysh, hipStream_t s) {
   hipStream_t s_ = s;
@@ -386,7 +386,7 @@ moe_status shared_ffn(const moe_config* cfg, const uint16_t* x, int T, const moe
   *ysh = at<float>(ws, L.ysh);
   return gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
                   ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
-                  at<void>(ws, L.hshs), *ysh, false, s);
+                  at<void>(ws, L.hshs), *ysh, true, s);
 }
 
 // moe_forward on a given workspace.  side_ok: a shared expert too small to
@@ -691,11 +691,12 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
     ysh = at<float>(ws, L.ysh);
     if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
                        ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
-                       at<void>(ws, L.hshs), ysh, false, stream)) != MOE_OK)
+                       at<void>(ws, L.hshs), ysh, true, stream)) != MOE_OK)
       return st;
   }
   HIP_TRY(joiner.join());
-  LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, false, T, K, H, out, stream));
+  // Y_perm and the shared output are bf16 here (the combine sums in fp32 and rounds once)
+  LAUNCH("combine", launch_combine(at<void>(ws, L.yperm), true, inv, w, ysh, true, T, K, H, out, stream));
   return MOE_OK;
 }
 
