@@ -36,8 +36,15 @@ FLAGS = [
 # block products with plain FMAs instead of copying each out of an AGPR, and
 # the operand registers go to the AGPRs (measured: routed gate/up 879 -> 826
 # us, down 532 -> 505 us at 4,096 tokens).
+# gemm2.hip: its 288 accumulator registers per lane (256 main + 32 for the
+# extra row block) exceed the 256 AGPRs; with matrix results in VGPRs the
+# compiler splits the accumulators over both files and keeps the operands in
+# AGPRs, where the AGPR form shuttled three blocks through a spare AGPR
+# range with copies and wait states around every use (2,048-token layer
+# 822 -> 754 us).
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
-         "gemm.hip": ["-Wno-inline-asm", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "gemm.hip": ["-Wno-inline-asm", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gemm2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

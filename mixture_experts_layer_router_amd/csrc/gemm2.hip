@@ -4,17 +4,25 @@
 //   C[r][n] = sum_k A[r][k] * B_e[n][k]   for the rows r of expert e's segment
 //
 // Tile: 256 rows x 256 B rows, 64 bytes of K per step, 4 waves each owning
-// 128 x 128 (4 x 4 blocks of 32x32).  Measured on MI355X, a CU moves about 64
-// bytes per clock from L2 into LDS when each load instruction covers whole
-// 128-byte row segments (8 rows x 128 B), but only about 32 when it covers
-// 16 rows x 64 B; this tile needs 32 bytes per clock at the full FP8 matrix
-// rate (a 128 x 256 tile needs 47).  So the loads move 128 bytes of each row,
-// two K steps, at a time: two LDS buffers of 64 KB (A and B, 256 rows x 128 B
-// each), double-buffered per step pair.  The loads of pair q+2 are issued
-// among the MFMAs of the odd step that starts pair q's second half, into the
-// buffer pair q has just released, and waited for two steps later.  Each lane
-// keeps two register sets of operands: the LDS reads of step s+1 go among
-// the MFMAs of step s.
+// 128 x 128 (4 x 4 blocks of 32x32), plus up to 32 extra rows (tile rows
+// 256-287, one 32-row block) when an expert's segment holds more than 256
+// rows: each wave computes that block against two of the B blocks it
+// already holds, so a 257-288-row segment streams its weight panel once
+// instead of running a second, nearly empty tile (a tile's time follows the
+// bytes it loads, so such a tail tile cost about half a full one).
+//
+// Measured on MI355X, a CU moves about 64 bytes per clock from L2 into LDS
+// when each load instruction covers whole 128-byte row segments (8 rows x
+// 128 B), but only about 32 when it covers 16 rows x 64 B; this tile needs
+// 32 bytes per clock at the full FP8 matrix rate (a 128 x 256 tile needs
+// 47).  So the loads move 128 bytes of each row, two K steps, at a time:
+// two LDS buffers (A 288 rows and B 256 rows x 128 B each), double-buffered
+// per step pair.  The loads of pair q+2 are issued among the MFMAs of the
+// odd step that starts pair q's second half, into the buffer pair q has just
+// released, and waited for two steps later.  The operand reads of step s+1
+// go among the MFMAs of step s: the A blocks and one B block into a second
+// register set, the other B blocks and the extra A block into the registers
+// they replace, right after their last MFMA of step s.
 //
 //   bf16   v_mfma_f32_32x32x16_bf16, two per block per step
 //   MXFP8  v_mfma_scale_f32_32x32x64_f8f6f4, one per block per step, with the
@@ -29,9 +37,16 @@
 // [32+16g, 48+16g) of the step, the instruction's K layout.
 //
 // MX scales (one e8m0 byte per 32 K of a row) are loaded once per 8 steps
-// (512 K): 16 bytes per row per load, into one of three LDS buffers, so the
+// (512 K): 16 bytes per row per load, into one of two LDS buffers, so the
 // scale loads add an eighth of the tile loads' cache-line requests instead of
-// matching them.  K must be a multiple of 512 (the host checks).
+// matching them.  Group g + 1 is loaded at step 8g into the buffer group g - 1
+// used; every wave finished reading group g - 1 before the barrier of step
+// 8g - 1.  K must be a multiple of 512 (the host checks).
+//
+// A wave of row half wm keeps B block j of its column half in its register
+// slot j ^ wm, so the extra block's operands are always slots 0 and 2
+// (compile-time register indices) and slots j, j + 2 still pair the same
+// columns of gate and up.
 //
 // EPI_GATEUP: B-tile rows [128w, 128w+64) are gate rows and [128w+64,
 // 128w+128) the up rows of the same 64 intermediate columns, so blocks j and
@@ -49,34 +64,49 @@ namespace {
 
 using namespace gemm_dev;
 
-constexpr int BM = kGemm2BM;  // 256 rows
-constexpr int BNT = 256;      // B rows per tile
-constexpr int BKB = 64;       // bytes of K per step
-constexpr int RB = 2 * BKB;   // bytes per LDS row: a step pair
-constexpr int kBufs = 2;      // LDS buffers (step pairs)
-constexpr int kLdsA = BM * RB;    // 32 KB
-constexpr int kLdsB = BNT * RB;   // 32 KB
-constexpr int kSG = 8;            // K steps per MX scale group (512 K)
-constexpr int kSBuf = 3;          // MX scale group buffers
-constexpr int kDPP = 16;          // tile loads per wave per step pair
+constexpr int BM = kGemm2BM;     // 256 main rows
+constexpr int BMX = kGemm2Rows;  // 288: main rows + the extra block
+constexpr int BNT = 256;         // B rows per tile
+constexpr int BKB = 64;          // bytes of K per step
+constexpr int RB = 2 * BKB;      // bytes per LDS row: a step pair
+constexpr int kBufs = 2;         // LDS buffers (step pairs)
+constexpr int kLdsA = BMX * RB;  // 36 KB
+constexpr int kLdsB = BNT * RB;  // 32 KB
+constexpr int kSG = 8;           // K steps per MX scale group (512 K)
+constexpr int kSBuf = 2;         // MX scale group buffers
+constexpr int kDPP = 17;         // tile loads per wave per step pair: 8 A, 8 B, 1 extra A
+static_assert(BMX - BM == 32, "the extra rows are one 32-row MFMA block");
 
+// Operands of one K step.  The A blocks, B register slot 3 and the A scales
+// are double-buffered: read among the first MFMAs of the step before.  B slots
+// 0-2, the extra A block and their scales are single-buffered: the MFMAs of a
+// step go B slot by B slot, and each slot's operands for the next step are
+// read right after that slot's last MFMA (slot 3 last, so it cannot wait).
 struct Frag {
   i32x8 a[4];  // [32-row block i]: chunk g | chunk 2+g of the step's 64 bytes
-  i32x8 b[4];  // [32-row B block j]
-  uint32_t sa[4], sb[4];  // MXFP8: e8m0 byte of the lane's row for its K block
+  i32x8 b3;    // B register slot 3 (B block 3 ^ wm)
+  uint32_t sa[4], sb3;  // MXFP8: e8m0 byte of the lane's row for its K block
+};
+struct Single {
+  i32x8 b[3];  // B register slots 0-2 (B blocks j ^ wm)
+  i32x8 ax;    // the extra 32-row block (tile rows 256-287)
+  uint32_t sb[3], sax;
 };
 
 template <int WF, int EPI>
 __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   constexpr bool MX = WF == W_MXFP8;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * (kLdsA + kLdsB)];
-  __shared__ __attribute__((aligned(16))) uint8_t sS[MX ? kSBuf : 1][2][MX ? BM * 16 : 16];
+  // MX scales: A rows (288, and 32 rows of room for the extra rows' 64-lane load) and B rows
+  __shared__ __attribute__((aligned(16))) uint8_t sSA[MX ? kSBuf : 1][MX ? (BMX + 32) * 16 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sSB[MX ? kSBuf : 1][MX ? BNT * 16 : 16];
 
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
+  int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int g = lane >> 5, l32 = lane & 31;
+  int g = lane >> 5, l32 = lane & 31;
   constexpr int nper = EPI == EPI_GATEUP ? BNT / 2 : BNT;  // output columns per tile
   const int KS = (EPI == EPI_F32 && p.ksplit > 1) ? p.ksplit : 1;
   const Tile tl = tile_of(p, BM, nper, KS);
@@ -108,27 +138,36 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
     oa[k] = PHYS_ROW(r) * lda_b + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
   const int na_blk = min(max((mrows - 64 * wave + 7) / 8, 0), 8);
+  // the extra rows: wave w loads tile rows 256 + 8w + [0, 8)
+  uint32_t oax;
+  {
+    const int r = BM + 8 * wave + (lane >> 3);
+    oax = PHYS_ROW(r) * lda_b + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
+  const bool ldx = mrows > BM + 8 * wave;  // this wave's extra load holds valid rows
+  const bool hasX = mrows > BM;            // the tile has extra rows
   // B: wave w loads tile B rows [64w, 64w+64); for EPI_GATEUP these are gate
   // rows (w even) or up rows (w odd) of intermediate columns n0 + 64 (w/2) + [0, 64)
+  // Block k's offset is formed at issue (a few VALU operations among the
+  // MFMAs) rather than kept in a register per block.
   const uint8_t* b_base;
-  uint32_t ob[8];
   {
     const void* bsrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1 : p.B0;
     b_base = uniform_ptr(static_cast<const uint8_t*>(bsrc) + size_t(e) * p.b_stride * esz<WF>());
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int t = 64 * wave + 8 * k + (lane >> 3);
-      const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + 8 * k + (lane >> 3) : min(n0 + t, N - 1);
-      ob[k] = uint32_t(br) * ldb_b + (((lane & 7) ^ ((t >> 1) & 7)) << 4);
-    }
   }
+  const int brow0 = (EPI == EPI_GATEUP ? n0 + 64 * wn : n0 + 64 * wave) + (lane >> 3);  // block 0's row
+  auto ob_of = [&](int k) {  // tile B row t = 64 wave + 8k + L/8: (t >> 1) & 7 = (4k + L/16) & 7
+    const int br = EPI == EPI_GATEUP ? brow0 + 8 * k : min(brow0 + 8 * k, N - 1);
+    return uint32_t(br) * ldb_b + (((lane & 7) ^ ((4 * k + (lane >> 4)) & 7)) << 4);
+  };
   // MX scales: wave w loads the 16 bytes of A rows and B rows [64w, 64w+64) of a group
   const uint8_t* as_base = nullptr;
   const uint8_t* bs_base = nullptr;
-  uint32_t oas = 0, obs = 0;
+  uint32_t oas = 0, obs = 0, oasx = 0;
   if constexpr (MX) {
     as_base = uniform_ptr(p.As);
     oas = PHYS_ROW(64 * wave + lane) * uint32_t(K / 32);
+    oasx = PHYS_ROW(BM + lane) * uint32_t(K / 32);  // wave 0 loads the extra rows' scales
     const void* ssrc = (EPI == EPI_GATEUP && (wave & 1)) ? p.B1s : p.B0s;
     bs_base = uniform_ptr(static_cast<const uint8_t*>(ssrc) + size_t(e) * p.bs_stride);
     const int br = EPI == EPI_GATEUP ? n0 + 64 * wn + lane : min(n0 + 64 * wave + lane, N - 1);
@@ -143,18 +182,32 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   // skipped there; the prologue (full) issues all 16, clamped to the last
   // pair, which keeps its wait count exact.
   auto tile_dma = [&](int d, int q, bool full) {
-    if (!full && (q >= npair || (d < 8 && d >= na_blk))) return;
+    if (!full && (q >= npair || (d < 8 && d >= na_blk))) return;  // (d == 16: see below)
     const int buf = q & 1, qq = min(q, npair - 1) + kp0;
-    if (d < 8) {
+    if (d == 16) {
+      if (!full && !ldx) return;
+      dma16(oax, a_base + size_t(qq) * RB, lds_a0 + buf * kLdsA + (BM + 8 * wave) * RB);
+    } else if (d < 8) {
       dma16(oa[d], a_base + size_t(qq) * RB, lds_a0 + buf * kLdsA + (64 * wave + 8 * d) * RB);
     } else {
-      dma16(ob[d - 8], b_base + size_t(qq) * RB, lds_b0 + buf * kLdsB + (64 * wave + 8 * (d - 8)) * RB);
+      dma16(ob_of(d - 8), b_base + size_t(qq) * RB, lds_b0 + buf * kLdsB + (64 * wave + 8 * (d - 8)) * RB);
     }
   };
-  auto scale_dma = [&](int q) {  // scale group q (clamped) into buffer q % 3
-    const int qq = min(q, ngroups - 1), buf = q % kSBuf;
-    dma16(oas, as_base + 16 * qq, lds_addr(&sS[buf][0][64 * wave * 16]));
-    dma16(obs, bs_base + 16 * qq, lds_addr(&sS[buf][1][64 * wave * 16]));
+  // scale group q (clamped) into buffer q % 2: 2 loads per wave, 3 in wave 0
+  auto scale_dma = [&](int q) {
+    if constexpr (MX) {
+      const int qq = min(q, ngroups - 1), buf = q % kSBuf;
+      dma16(oas, as_base + 16 * qq, lds_addr(&sSA[buf][64 * wave * 16]));
+      dma16(obs, bs_base + 16 * qq, lds_addr(&sSB[buf][64 * wave * 16]));
+      if (wave == 0) dma16(oasx, as_base + 16 * qq, lds_addr(&sSA[buf][BM * 16]));
+    }
+  };
+  // wait for every load but the scale loads issued last
+  auto wait_but_scales = [&]() {
+    if (wave == 0)
+      wait_vm<3>();
+    else
+      wait_vm<2>();
   };
 
   // LDS operand reads: block i of the lane's rows, chunks 4h+g and 4h+2+g
@@ -162,110 +215,177 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   // the wave's A row blocks interleave with the other row half's: block i
   // covers tile rows 64 i + 32 wm + [0, 32), so a partial tile's blocks are
   // shared by both halves
-  const int rowA = (32 * wm + l32) * RB, rowB = (128 * wn + l32) * RB;
-  const int srowA = (32 * wm + l32) * 16 + g, srowB = (128 * wn + l32) * 16 + g;
-  constexpr int NR = 16 + (MX ? 8 : 0);  // LDS reads per step
-  auto read_op = [&](int r, Frag& fr, int t) {  // read r of step t's operands
+  const int rowA = (32 * wm + l32) * RB, rowB = (128 * wn + l32) * RB, rowX = (BM + l32) * RB;
+  const int srowA = (32 * wm + l32) * 16 + g, srowB = (128 * wn + l32) * 16 + g, srowX = (BM + l32) * 16 + g;
+  // A buffer, B buffer, the two chunk offsets and the scale byte of step t
+  struct StepAddr {
+    const uint8_t *As, *Bs;
+    int colo0, colo1, sbuf, byte;
+  };
+  auto addr_of = [&](int t) {
     const int buf = (t >> 1) & 1, h = t & 1;
-    const uint8_t* As_ = smem + buf * kLdsA;
-    const uint8_t* Bs_ = smem + kBufs * kLdsA + buf * kLdsB;
-    const int colo0 = ((4 * h + g) ^ f) << 4, colo1 = ((4 * h + 2 + g) ^ f) << 4;
+    return StepAddr{smem + buf * kLdsA, smem + kBufs * kLdsA + buf * kLdsB, ((4 * h + g) ^ f) << 4,
+                    ((4 * h + 2 + g) ^ f) << 4, (t / kSG) % kSBuf, 2 * (t % kSG)};
+  };
+  auto rd = [&](const uint8_t* base, int hi, const StepAddr& sa) {
+    return *reinterpret_cast<const i32x4*>(base + (hi ? sa.colo1 : sa.colo0));
+  };
+  // double-buffered read r of step t's operands
+  constexpr int ND = 10 + (MX ? 5 : 0);
+  auto read_dbl = [&](int r, Frag& fr, int t) {
+    const StepAddr sa = addr_of(t);
     if (r < 8) {
-      const int i = r / 2;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(As_ + rowA + 64 * RB * i + ((r & 1) ? colo1 : colo0));
+      const i32x4 v = rd(sa.As + rowA + 64 * RB * (r / 2), r & 1, sa);
       if (r & 1)
-        fr.a[i].hi = v;
+        fr.a[r / 2].hi = v;
       else
-        fr.a[i].lo = v;
-    } else if (r < 16) {
-      const int j = (r - 8) / 2;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(Bs_ + rowB + 32 * RB * j + ((r & 1) ? colo1 : colo0));
+        fr.a[r / 2].lo = v;
+    } else if (r < 10) {
+      const i32x4 v = rd(sa.Bs + rowB + 32 * RB * (3 ^ wm), r & 1, sa);
       if (r & 1)
-        fr.b[j].hi = v;
+        fr.b3.hi = v;
       else
-        fr.b[j].lo = v;
+        fr.b3.lo = v;
     } else if constexpr (MX) {
-      const int buf = (t / kSG) % kSBuf, byte = 2 * (t % kSG);
-      if (r < 20)
-        fr.sa[r - 16] = sS[buf][0][srowA + 64 * 16 * (r - 16) + byte];
+      if (r < 14)
+        fr.sa[r - 10] = sSA[sa.sbuf][srowA + 64 * 16 * (r - 10) + sa.byte];
       else
-        fr.sb[r - 20] = sS[buf][1][srowB + 32 * 16 * (r - 20) + byte];
+        fr.sb3 = sSB[sa.sbuf][srowB + 32 * 16 * (3 ^ wm) + sa.byte];
+    }
+  };
+  // single-buffered reads of B slot j (and, with slot 2, the extra block) for step t
+  auto read_single = [&](int j, Single& sg, int t) {
+    const StepAddr sa = addr_of(t);
+    sg.b[j].lo = rd(sa.Bs + rowB + 32 * RB * (j ^ wm), 0, sa);
+    sg.b[j].hi = rd(sa.Bs + rowB + 32 * RB * (j ^ wm), 1, sa);
+    if constexpr (MX) sg.sb[j] = sSB[sa.sbuf][srowB + 32 * 16 * (j ^ wm) + sa.byte];
+    if (j == 2 && hasX) {
+      sg.ax.lo = rd(sa.As + rowX, 0, sa);
+      sg.ax.hi = rd(sa.As + rowX, 1, sa);
+      if constexpr (MX) sg.sax = sSA[sa.sbuf][srowX + sa.byte];
     }
   };
 
   // this wave's blocks that hold valid rows (block i is tile block 2 i + wm): blocks at or past nI are skipped
   const int nI = min(max(((mrows + 31) / 32 - wm + 1) / 2, 0), 4);
-  f32x16 acc[4][4];
+  f32x16 acc[4][4], accx[2];  // accx[x]: the extra block against register slot 2x
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // MFMA m of a step.  bf16: K half outermost, so the two MFMAs on one
-  // accumulator are 16 instructions apart.  In the first step each
-  // accumulator's first MFMA starts from zero.
-  constexpr int NM = MX ? 16 : 32;
-  auto mfma_op = [&](int m, const Frag& fr, auto first_t) {
-    const int q = m / 16, i = (m / 4) % 4, j = m % 4;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accx[x][r] = 0.f;
+  // One MFMA: block (i, slot j) or the extra block against slot 2x, K half q
+  // (bf16: two per block per step).  In the first step each accumulator's
+  // first MFMA starts from zero.
+  constexpr int QN = MX ? 1 : 2;   // MFMAs per block per step
+  constexpr int NM = 18 * QN;      // MFMA slots per step: 16 blocks + 2 extra
+  auto mfma_main = [&](int i, int j, int q, const Frag& cur, const Single& sg, auto first_t) {
     if (i >= nI) return;
+    const i32x8& b = j == 3 ? cur.b3 : sg.b[j];
     f32x16 c = acc[i][j];
     if (decltype(first_t)::value && q == 0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) c[r] = 0.f;
     }
     if constexpr (MX) {
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr.a[i], fr.b[j], c, 0, 0, 0, int(fr.sa[i]), 0,
-                                                                  int(fr.sb[j]));
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], b, c, 0, 0, 0, int(cur.sa[i]), 0,
+                                                                  int(j == 3 ? cur.sb3 : sg.sb[j]));
     } else {
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(q ? fr.a[i].hi : fr.a[i].lo),
-                                                          as_bf16(q ? fr.b[j].hi : fr.b[j].lo), c, 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(q ? cur.a[i].hi : cur.a[i].lo),
+                                                          as_bf16(q ? b.hi : b.lo), c, 0, 0, 0);
+    }
+  };
+  auto mfma_x = [&](int x, int q, const Single& sg, auto first_t) {
+    if (!hasX) return;
+    f32x16 c = accx[x];
+    if (decltype(first_t)::value && q == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[r] = 0.f;
+    }
+    if constexpr (MX) {
+      accx[x] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sg.ax, sg.b[2 * x], c, 0, 0, 0, int(sg.sax), 0,
+                                                                int(sg.sb[2 * x]));
+    } else {
+      accx[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(q ? sg.ax.hi : sg.ax.lo),
+                                                        as_bf16(q ? sg.b[2 * x].hi : sg.b[2 * x].lo), c, 0, 0, 0);
     }
   };
 
-  // step s: MFMAs on cur (read during step s-1) interleaved with the LDS reads
-  // of step s+1 into nxt.  An odd step s = 2q+1 first waits for pair q+1 (read
-  // from step s on) and then, pair q's buffer being released by every wave,
-  // issues the loads of pair q+2 into it.  MX scale groups are loaded at the
-  // steps = 0 mod 8.  Loads complete in issue order, so the wait leaves out
-  // exactly the scale loads issued at step s-1 (at step 1, the step-1 case
-  // is peeled at compile time).
-  auto step = [&](int s, Frag& cur, Frag& nxt, auto first_t, auto odd_t, auto step1_t) {
+  // step s: the MFMAs on cur and sg (slot by slot: the 4 blocks of slot j,
+  // after slots 0 and 2 the extra block), with the double-buffered reads of
+  // step s+1 into nxt among the first half of them and each single-buffered
+  // slot re-read for step s+1 after its last MFMA.  An odd step s = 2q+1 first
+  // waits for pair q+1 (read from step s on) and then, pair q's buffer being
+  // released by every wave, issues the loads of pair q+2 into it, one per
+  // MFMA.  MX scale groups are loaded at the steps = 0 mod 8.  Loads complete
+  // in issue order, so the wait leaves out exactly the scale loads issued at
+  // step s-1 (at step 1, the step-1 case is peeled at compile time).
+  auto step = [&](int s, Frag& cur, Frag& nxt, Single& sg, auto first_t, auto odd_t, auto step1_t) {
     constexpr bool odd = decltype(odd_t)::value;
-    wait_lgkm0();  // cur is in registers: this wave no longer reads step s's half
+    wait_lgkm0();  // this wave no longer reads step s's half
     if constexpr (odd) {
-      if constexpr (decltype(step1_t)::value)
-        wait_vm<MX ? 2 : 0>();
-      else if (MX && ((s - 1) & (kSG - 1)) == 0)
-        wait_vm<2>();
-      else
+      if constexpr (decltype(step1_t)::value) {
+        if constexpr (MX)
+          wait_but_scales();
+        else
+          wait_vm<0>();
+      } else if (MX && ((s - 1) & (kSG - 1)) == 0) {
+        wait_but_scales();
+      } else {
         wait_vm<0>();
+      }
       barrier();  // every wave's loads of pair q+1 have landed; pair q's buffer is free
     } else {
       if (MX && (s & (kSG - 1)) == 0) scale_dma(s / kSG + 1);
     }
     const int q2 = (s >> 1) + 2;
-    // the reads go among the first half of the MFMAs, so they have landed
-    // when the next step starts; the loads of an odd step go one per MFMA
     constexpr int NH = NM / 2;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      mfma_op(m, cur, first_t);
-      __builtin_amdgcn_sched_barrier(0);
+    int m = 0;  // MFMA slot (compile-time after unrolling)
+    auto after = [&](int m) {
       if (m < NH) {
 #pragma unroll
-        for (int r = (m * NR) / NH; r < ((m + 1) * NR) / NH; ++r) read_op(r, nxt, s + 1);
+        for (int r = (m * ND) / NH; r < ((m + 1) * ND) / NH; ++r) read_dbl(r, nxt, s + 1);
       }
       if constexpr (odd) {
 #pragma unroll
         for (int d = (m * kDPP) / NM; d < ((m + 1) * kDPP) / NM; ++d) tile_dma(d, q2, false);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int q = 0; q < QN; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mfma_main(i, j, q, cur, sg, first_t);
+          __builtin_amdgcn_sched_barrier(0);
+          after(m++);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if (j == 0 || j == 2) {
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+          mfma_x(j / 2, q, sg, first_t);
+          __builtin_amdgcn_sched_barrier(0);
+          after(m++);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (j < 3) {
+        read_single(j, sg, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
   // ------------------------------------------------------------ main loop
   Frag f0, f1;
+  Single sg;
   if constexpr (MX) scale_dma(0);
 #pragma unroll
   for (int q = 0; q < kBufs; ++q)
@@ -274,29 +394,34 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   wait_vm<kDPP>();  // pair 0 and scale group 0 (the loads of pair 1 may be in flight)
   barrier();
 #pragma unroll
-  for (int r = 0; r < NR; ++r) read_op(r, f0, 0);
+  for (int r = 0; r < ND; ++r) read_dbl(r, f0, 0);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) read_single(j, sg, 0);
   const std::false_type no{};
   const std::true_type yes{};
-  step(0, f0, f1, yes, no, no);
-  step(1, f1, f0, no, yes, yes);  // nk >= 2
+  step(0, f0, f1, sg, yes, no, no);
+  step(1, f1, f0, sg, no, yes, yes);  // nk >= 2
   for (int s = 2; s + 1 < nk; s += 2) {  // nk is even: steps come in (even, odd) pairs
-    step(s, f0, f1, no, no, no);
-    step(s + 1, f1, f0, no, yes, no);
+    step(s, f0, f1, sg, no, no, no);
+    step(s + 1, f1, f0, sg, no, yes, no);
   }
   wait_vm<0>();
   wait_lgkm0();
   barrier();  // the buffers are free for the epilogue
 
   // ------------------------------------------------------------ epilogue
-  // lane l holds column l%32 of each 32x32 block, rows 8(r/4) + 4(l/32) + r%4
-  auto row_of = [&](int i, int r) { return 64 * i + 32 * wm + 8 * (r >> 2) + 4 * g + (r & 3); };
+  // lane l holds column l%32 of each 32x32 block, rows 8(r/4) + 4(l/32) + r%4.
+  // The lane index is re-derived here behind an empty asm, so the compiler
+  // cannot hoist the epilogue's per-lane addresses above the K loop, where
+  // they would hold registers through it.
+  {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    lane = l;
+    g = l >> 5;
+    l32 = l & 31;
+  }
   if constexpr (EPI == EPI_GATEUP) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][jj][r] = silu(acc[i][jj][r]) * acc[i][jj + 2][r];
     // Stage the wave's h (128 rows x 64 columns, fp32) through LDS, 64 rows
     // at a time, so that each lane finishes whole 32-column row blocks in
     // registers: the MX block maximum without cross-lane reductions, and
@@ -306,6 +431,57 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
     float* wsf = reinterpret_cast<float*>(smem) + wave * (64 * RSF);
     const int cb = n0 + 64 * wn;  // first h column of this wave
     const int omode = p.C_f32 ? 0 : (p.out_afmt == A_NONE ? 1 : 2);
+    // store 32 consecutive h values of tile row rl from column col
+    auto store_h = [&](int rl, int col, const f32x4 (&v)[8]) {
+      const size_t orow = size_t(seg0 + m0 + rl);
+      if (omode == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) *reinterpret_cast<f32x4*>(p.C_f32 + orow * p.ldc + col + 4 * q) = v[q];
+      } else if (omode == 1) {
+        uint16_t* dst = static_cast<uint16_t*>(p.C) + orow * p.ldc + col;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          i32x4 o;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x4& x = v[2 * q + t / 2];
+            const int c = 2 * (t & 1);
+            o[t] = int(uint32_t(f32_to_bf16(x[c])) | (uint32_t(f32_to_bf16(x[c + 1])) << 16));
+          }
+          *reinterpret_cast<i32x4*>(dst + 8 * q) = o;
+        }
+      } else {  // MXFP8 1x32: this lane's 32 values are one block
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[q][0]), fabsf(v[q][1])), fmaxf(fabsf(v[q][2]), fabsf(v[q][3]))));
+        const int xe = mx_exponent(amax);
+        uint8_t* dst = static_cast<uint8_t*>(p.C) + orow * p.ldc + col;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          i32x4 o;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x4& x = v[4 * q2 + t];
+            o[t] = int(e4m3x4_sat(__builtin_amdgcn_ldexpf(x[0], -xe), __builtin_amdgcn_ldexpf(x[1], -xe),
+                                  __builtin_amdgcn_ldexpf(x[2], -xe), __builtin_amdgcn_ldexpf(x[3], -xe)));
+          }
+          *reinterpret_cast<i32x4*>(dst + 16 * q2) = o;
+        }
+        static_cast<uint8_t*>(p.Cs)[orow * (N / 32) + col / 32] = uint8_t(xe + 127);
+      }
+    };
+    // the extra rows: h of tile rows 256-287, the wave's column block wm;
+    // lane l < 32 finishes row 256 + l
+    if (hasX) {  // first, so the extra accumulators are free before the main blocks
+#pragma unroll
+      for (int r = 0; r < 16; ++r) wsf[(8 * (r >> 2) + 4 * g + (r & 3)) * RSF + l32] = silu(accx[0][r]) * accx[1][r];
+      f32x4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const f32x4*>(wsf + l32 * RSF + 4 * q);
+      if (lane < 32 && BM + lane < mrows) store_h(BM + lane, cb + 32 * wm, v);
+    }
+    // register slot jj holds the wave's h column block jj ^ wm
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -314,7 +490,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            wsf[(32 * ii + 8 * (r >> 2) + 4 * g + (r & 3)) * RSF + 32 * jj + l32] = acc[2 * h + ii][jj][r];
+            wsf[(32 * ii + 8 * (r >> 2) + 4 * g + (r & 3)) * RSF + 32 * (jj ^ wm) + l32] =
+                silu(acc[2 * h + ii][jj][r]) * acc[2 * h + ii][jj + 2][r];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int b = lane + 64 * k, row = b >> 1, half = b & 1;
@@ -322,45 +499,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
         f32x4 v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const f32x4*>(wsf + row * RSF + 32 * half + 4 * q);
-        if (rl >= mrows) continue;
-        const size_t orow = size_t(seg0 + m0 + rl);
-        const int col = cb + 32 * half;
-        if (omode == 0) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) *reinterpret_cast<f32x4*>(p.C_f32 + orow * p.ldc + col + 4 * q) = v[q];
-        } else if (omode == 1) {
-          uint16_t* dst = static_cast<uint16_t*>(p.C) + orow * p.ldc + col;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            i32x4 o;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const f32x4& x = v[2 * q + t / 2];
-              const int c = 2 * (t & 1);
-              o[t] = int(uint32_t(f32_to_bf16(x[c])) | (uint32_t(f32_to_bf16(x[c + 1])) << 16));
-            }
-            *reinterpret_cast<i32x4*>(dst + 8 * q) = o;
-          }
-        } else {  // MXFP8 1x32: this lane's 32 values are one block
-          float amax = 0.f;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[q][0]), fabsf(v[q][1])), fmaxf(fabsf(v[q][2]), fabsf(v[q][3]))));
-          const int xe = mx_exponent(amax);
-          uint8_t* dst = static_cast<uint8_t*>(p.C) + orow * p.ldc + col;
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            i32x4 o;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const f32x4& x = v[4 * q2 + t];
-              o[t] = int(e4m3x4_sat(__builtin_amdgcn_ldexpf(x[0], -xe), __builtin_amdgcn_ldexpf(x[1], -xe),
-                                    __builtin_amdgcn_ldexpf(x[2], -xe), __builtin_amdgcn_ldexpf(x[3], -xe)));
-            }
-            *reinterpret_cast<i32x4*>(dst + 16 * q2) = o;
-          }
-          static_cast<uint8_t*>(p.Cs)[orow * (N / 32) + col / 32] = uint8_t(xe + 127);
-        }
+        if (rl < mrows) store_h(rl, cb + 32 * half, v);
       }
     }
   } else {
@@ -371,23 +510,24 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
     constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row
     uint8_t* ws = smem + wave * (32 * RS);
     const int cw = n0 + 128 * wn;  // first output column of this wave
+    // stage one 32x32 block for column block cb
+    auto stage = [&](const f32x16& a, int cb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          uint8_t* d = ws + (8 * (r >> 2) + 4 * g + (r & 3)) * RS + (32 * j + l32) * ES;
-          if (EPI == EPI_F32)
-            *reinterpret_cast<float*>(d) = acc[i][j][r];
-          else
-            *reinterpret_cast<uint16_t*>(d) = f32_to_bf16(acc[i][j][r]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        uint8_t* d = ws + (8 * (r >> 2) + 4 * g + (r & 3)) * RS + (32 * cb + l32) * ES;
+        if (EPI == EPI_F32)
+          *reinterpret_cast<float*>(d) = a[r];
+        else
+          *reinterpret_cast<uint16_t*>(d) = f32_to_bf16(a[r]);
+      }
+    };
+    // store the staged rows row0 + [0, 32) (the column blocks in cmask)
+    auto store_rows = [&](int row0, int cmask) {
 #pragma unroll 4
       for (int c = lane; c < 32 * CPR; c += 64) {
         const int rl = c / CPR, cc = c % CPR;
-        const int row = 64 * i + 32 * wm + rl;
-        if (row >= mrows) continue;
+        const int row = row0 + rl;
+        if (row >= mrows || !((cmask >> (cc * (16 / ES) / 32)) & 1)) continue;
         const int col = cw + cc * (16 / ES);
         const i32x4 v = *reinterpret_cast<const i32x4*>(ws + rl * RS + cc * 16);
         const size_t orow = size_t(seg0 + m0 + row);
@@ -399,6 +539,18 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
             for (int b = 0; b < ES; ++b) dst[q * ES + b] = reinterpret_cast<const uint8_t*>(&v)[q * ES + b];
         }
       }
+    };
+    if (hasX) {  // the extra rows: column blocks wm (slot 0) and 2 + wm (slot 2)
+      stage(accx[0], wm);
+      stage(accx[1], 2 + wm);
+      store_rows(BM, (1 << wm) | (4 << wm));
+    }
+    // register slot j holds the wave's column block j ^ wm
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) stage(acc[i][j], j ^ wm);
+      store_rows(64 * i + 32 * wm, 0xf);
     }
   }
 }

@@ -81,9 +81,8 @@ MOE_DEV Tile tile_of(const GemmParams& p, int bm, int nper, int ks) {
     if (p.tiles) {
       e = p.tiles[2 * pe];
       const int c0 = min(max(p.seg[e], 0), p.M), c1 = min(max(p.seg[e + 1], c0), p.M);
-      step = tile_step(c1 - c0, bm);
+      ne = max(tile_split(c1 - c0, bm, &step), 1);
       be = pe - p.tiles[2 * pe + 1] / step;
-      ne = max((c1 - c0 + bm - 1) / bm, 1);
     }
     const int local = idx - be * NB;
     if (p.tiles) {  // one expert's m-tiles of an n-block are adjacent

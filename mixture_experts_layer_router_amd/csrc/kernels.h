@@ -72,20 +72,52 @@ hipError_t launch_permute_scatter(const int* ids, int TK, int E, const int* hist
 hipError_t launch_validate_dispatch(const int* ids, int TK, int E, const int* offsets, const int* perm, const int* inv,
                                    const int* tiles, const int* ntiles, int maxt, int bm, int* flags, hipStream_t s);
 hipError_t launch_build_tiles(const int* offsets, int E, int rows, int bm, int* tiles, int* ntiles, hipStream_t s);
+constexpr int kGemmBM = 128;   // rows per tile of the 128-row grouped GEMM (gemm.hip)
+constexpr int kGemm2BM = 256;  // main rows per tile of the large-tile grouped GEMM (gemm2.hip)
 inline int max_tiles(int rows, int E, int bm) { return (rows + bm - 1) / bm + E; }
-// Row offset step of one expert's grouped-GEMM tiles: an expert with cnt rows
-// gets ceil(cnt / bm) tiles.  For the 256-row kernel they share the rows
-// evenly in multiples of 32 (one MFMA row block), so 272 rows run as 160 + 112
-// rather than 256 + 16: a tile whose row blocks are spread over both halves of
-// the workgroup's waves takes time in proportion to its blocks, while a
-// 16-row tail costs about half a full tile in its latency-bound K loop.  The
-// 128-row kernel keeps tiles of bm rows (its waves hold 2 blocks each, so an
-// even split gains nothing).  Every tile holds at least one row.
-__host__ __device__ inline int tile_step(int cnt, int bm) {
-  const int n = (cnt + bm - 1) / bm;
-  if (bm < 256 || n <= 1) return bm;
+// Rows one tile of the large-tile kernel can hold: its 256 main rows plus one
+// extra 32-row MFMA block, which the waves compute against the B operands
+// they already hold.
+constexpr int kGemm2Rows = 288;
+// Number of tiles and row offset step of one expert's grouped-GEMM tiles.
+// 128-row kernel: ceil(cnt / bm) tiles of bm rows.  Large-tile kernel: an
+// expert of at most kGemm2Rows rows is one tile (so the 256 +- 16 rows of a
+// flat 2,048-token layer stream each weight panel once, where a 256-row tile
+// plus a 16-row tail streamed it twice: a tail tile is bound by its weight
+// loads, not its MFMAs); larger experts get ceil(cnt / kGemm2Rows) tiles that
+// share the rows evenly in multiples of 32 (one MFMA row block), so 600 rows
+// run as 224 + 224 + 152.  Every tile holds at least one row; where an even
+// split cannot guarantee that, the tiles fall back to 256-row steps.
+__host__ __device__ inline int tile_split(int cnt, int bm, int* step) {
+  if (cnt <= 0) {
+    *step = bm;
+    return 0;
+  }
+  if (bm != kGemm2BM) {
+    *step = bm;
+    return (cnt + bm - 1) / bm;
+  }
+  const int n = (cnt + kGemm2Rows - 1) / kGemm2Rows;
+  if (n == 1) {
+    *step = kGemm2Rows;
+    return 1;
+  }
   const int h = ((cnt + n - 1) / n + 31) / 32 * 32;
-  return (h >= bm || (n - 1) * h >= cnt) ? bm : h;
+  if ((n - 1) * h < cnt) {
+    *step = h;
+    return n;
+  }
+  *step = bm;
+  return (cnt + bm - 1) / bm;
+}
+__host__ __device__ inline int tile_count(int cnt, int bm) {
+  int step;
+  return tile_split(cnt, bm, &step);
+}
+__host__ __device__ inline int tile_step(int cnt, int bm) {
+  int step;
+  tile_split(cnt, bm, &step);
+  return step;
 }
 
 // ------------------------------------------------------------------ quantisers
@@ -140,8 +172,6 @@ struct GemmParams {
   // a tile list the launcher picks the kernel (gemm2_chosen).
   int bm;
 };
-constexpr int kGemmBM = 128;
-constexpr int kGemm2BM = 256;
 constexpr int kGemmMaxK = 8192;  // FP8_B128 GEMM: K (elements) <= this
 hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, hipStream_t s);
 // large-tile kernel: bf16, and MXFP8 with K a multiple of 512

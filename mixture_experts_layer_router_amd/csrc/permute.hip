@@ -58,7 +58,7 @@ MOE_DEV void scan_experts(const int* cnt, int E, int* out_lds, int* out_glob) {
 }
 
 MOE_DEV void write_tiles(const int* cnt, int E, int bm, int* tiles, int* ntiles, int* scratch) {
-  // scratch[e] = exclusive prefix of ceil(cnt/bm); wave 0 scans, all threads write
+  // scratch[e] = exclusive prefix of the experts' tile counts; wave 0 scans, all threads write
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
@@ -66,7 +66,7 @@ MOE_DEV void write_tiles(const int* cnt, int E, int bm, int* tiles, int* ntiles,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int e = lane * 4 + i;
-      v[i] = e < E ? (cnt[e] + bm - 1) / bm : 0;
+      v[i] = e < E ? tile_count(cnt[e], bm) : 0;
       sum += v[i];
     }
     int incl = wave_incl_scan(sum);
@@ -81,7 +81,8 @@ MOE_DEV void write_tiles(const int* cnt, int E, int bm, int* tiles, int* ntiles,
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
-    const int n = (cnt[e] + bm - 1) / bm, b = scratch[e], step = tile_step(cnt[e], bm);
+    int step;
+    const int n = tile_split(cnt[e], bm, &step), b = scratch[e];
     for (int i = 0; i < n; ++i) {
       tiles[2 * (b + i)] = e;
       tiles[2 * (b + i) + 1] = i * step;
@@ -219,8 +220,8 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int* __restrict_
 // offsets[E] != TK, bit 2 for an id outside [0, E), bit 3 if perm_src is not
 // a bijection of [0, TK) with inv_pos its inverse, bit 4 if a position holds
 // a slot of another expert or a segment is not in ascending slot order, bit
-// 5 if the tile list does not cover each segment in order with ceil(cnt /
-// bm) tiles at the row step tile_step(cnt, bm).
+// 5 if the tile list does not cover each segment in order with
+// tile_count(cnt, bm) tiles at the row step tile_step(cnt, bm).
 __global__ __launch_bounds__(256) void validate_dispatch_kernel(const int* __restrict__ ids, int TK, int E,
                                                                 const int* __restrict__ off,
                                                                 const int* __restrict__ perm,
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256) void validate_dispatch_kernel(const int* __res
     if (e == 0 && off[0] != 0) bits |= 1;
     if (e < E && off[e] > off[e + 1]) bits |= 1;
     if (e == E && off[E] != TK) bits |= 2;
-    if (e < E) want += (max(off[e + 1] - off[e], 0) + bm - 1) / bm;
+    if (e < E) want += tile_count(max(off[e + 1] - off[e], 0), bm);
   }
   for (int i = tid; i < TK; i += 256) {
     const int id = ids[i];

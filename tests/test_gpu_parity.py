@@ -288,7 +288,11 @@ def _check_dispatch(cfg, layer, r):
     n = int(moe.ws_region(c, T, layer.ws, "ntiles", 1).cpu().numpy()[0])
     tiles = moe.ws_region(c, T, layer.ws, "tiles", 2 * n).cpu().numpy().reshape(n, 2)
     cnt = np.diff(r.offsets)
-    want = sorted((e, i * _tile_step(int(cnt[e]), bm)) for e in range(E) for i in range(-(-int(cnt[e]) // bm)))
+    want = []
+    for e in range(E):
+        n, step = _tile_split(int(cnt[e]), bm)
+        want += [(e, i * step) for i in range(n)]
+    want.sort()
     assert sorted(map(tuple, tiles.tolist())) == want
     # every row of every segment in exactly one tile
     for e in range(E):
@@ -297,14 +301,23 @@ def _check_dispatch(cfg, layer, r):
         assert all(0 <= a < b <= int(cnt[e]) for a, b in zip(starts, ends)) and (not starts or starts[0] == 0)
 
 
-def _tile_step(cnt, bm):
-    """Row offset between one expert's tiles: ceil(cnt/bm) tiles; for 256-row
-    tiles the rows are shared evenly in multiples of 32 (each tile non-empty)."""
-    n = -(-cnt // bm)
-    if bm < 256 or n <= 1:
-        return bm
+def _tile_split(cnt, bm):
+    """(tiles, row step) of one expert's grouped-GEMM tiles.  128-row kernel:
+    ceil(cnt/bm) tiles of bm rows.  Large-tile kernel (256 main rows + one
+    extra 32-row block): up to 288 rows in one tile; more rows in
+    ceil(cnt/288) tiles sharing them evenly in multiples of 32, each tile
+    non-empty (else 256-row steps)."""
+    if cnt <= 0:
+        return 0, bm
+    if bm != 256:
+        return -(-cnt // bm), bm
+    n = -(-cnt // 288)
+    if n == 1:
+        return 1, 288
     h = (-(-cnt // n) + 31) // 32 * 32
-    return bm if (h >= bm or (n - 1) * h >= cnt) else h
+    if (n - 1) * h < cnt:
+        return n, h
+    return -(-cnt // 256), 256
 
 
 @pytest.mark.parametrize("cfgname", [c.name for c in synth.CONFIGS])
@@ -334,22 +347,37 @@ def test_forward_full_size(cfgname):
         _check_dispatch(cfg, layer, r)
 
 
-# A mid-size MXFP8 layer whose H and I are multiples of 512, so its routed
-# FFN runs on the 256-row kernel, with about 300 rows per expert: every
-# expert has a full tile and a ragged tail tile.
-MX_MID = small_cfg(3, tokens=600, hidden=1024, n_experts=8, inter=512, shared_inter=512)
+# Mid-size layers whose routed FFN runs on the large-tile kernel (MXFP8 with
+# H and I multiples of 512, or bf16): about 300 rows per expert (most experts
+# split over two tiles), and 256-280 rows per expert (experts that use the
+# tile's extra 32-row block beside experts of at most 256 rows or experts split
+# over two tiles).
+MID = {
+    "mx_8exp_600tok": small_cfg(3, tokens=600, hidden=1024, n_experts=8, inter=512, shared_inter=512),
+    "mx_8exp_512tok": small_cfg(3, tokens=512, hidden=1024, n_experts=8, inter=512, shared_inter=512),
+    "mx_8exp_560tok": small_cfg(3, tokens=560, hidden=1024, n_experts=8, inter=512, shared_inter=512),
+    "bf16_8exp_512tok": small_cfg(0, tokens=512, hidden=512, n_experts=8, n_groups=1, topk_groups=1, topk=4,
+                                  inter=256, shared_inter=256),
+    "bf16_8exp_560tok": small_cfg(0, tokens=560, hidden=512, n_experts=8, n_groups=1, topk_groups=1, topk=4,
+                                  inter=256, shared_inter=256),
+}
 
 
-def test_forward_mid_size_mx_large_tiles():
-    cfg = MX_MID
+@pytest.mark.parametrize("name", list(MID))
+def test_forward_mid_size_large_tiles(name):
+    cfg = MID[name]
     inp = gpu_inputs(cfg)
     layer = moe.Layer(cfg, inp)
     assert moe.ffn_tile_rows(layer.cfg, 0) == 256 and moe.ffn_tile_rows(layer.cfg, 1) == 256
-    say("[forward mid mx]")
+    say(f"[forward mid] {name}")
     out, ids, w = _forward(cfg, inp, layer=layer)
     r = oracle.forward(cfg, inp.x, inp.w_router, inp.bias, inp.routed, inp.shared)
     cnt = np.diff(r.offsets)
-    assert ((cnt > 256) & (cnt % 256 != 0)).sum() >= 4, cnt   # full tiles plus ragged tails
+    if name == "mx_8exp_600tok":
+        assert (cnt > 288).sum() >= 4, cnt   # experts split over two tiles
+    else:
+        assert ((cnt > 256) & (cnt <= 288)).sum() >= 2, cnt   # the extra 32-row block
+        assert ((cnt <= 256) | (cnt > 288)).sum() >= 1, cnt    # next to plain or split experts
     assert np.array_equal(ids.cpu().numpy(), r.ids)
     assert rel_err(oracle.bf16_to_f64(out), r.out) <= TOL
     _check_dispatch(cfg, layer, r)
