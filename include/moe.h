@@ -224,17 +224,18 @@ moe_status moe_combine(const moe_config* cfg /*host*/, const float* y_perm, cons
  * and one weight format for routed and shared experts runs as ONE
  * persistent launch (the DSV2-236B-MegaKernel README's single-launch idea,
  * "What runs inside the single launch"): workgroups take router rows,
- * shared gate/up, routed gate/up and down+combine items in that order from
- * queues in the workspace, and wait (bounded) only for earlier items.
- * Waits give up after about 0.2 s: int32 word 0 of the workspace then
- * becomes nonzero (sticky; moe_workspace_check reports and clears it) and
- * the rows of `out` written by the workgroup that gave up are NaN.  With the
- * device to itself a wait lasts microseconds.  Progress needs at least
- * max(E, 32) of the launch's workgroups resident at once (the first E take
- * the router rows, and each of 32 queues needs a resident server); the
- * launch asks for the device's full resident capacity, so only a kernel on
- * another stream that holds most of the CUs for longer than the wait bound
- * can make a wait give up.  Other T <= 4 cases run in four to six launches
+ * shared gate/up, routed gate/up and down+combine items in that order (a
+ * static round robin when there are at most 16 items per workgroup, else
+ * claimed from queues in the workspace), and wait (bounded) only for earlier
+ * items.  Waits give up after about 0.2 s: int32 word 0 of the workspace
+ * then becomes nonzero (sticky; moe_workspace_check reports and clears it)
+ * and the rows of `out` written by the workgroup that gave up are NaN.  With
+ * the device to itself a wait lasts microseconds.  Progress needs every
+ * workgroup of the launch to become resident (static round robin: each owns
+ * a fixed share of the items) or max(E, 32) of them resident at once
+ * (claims); the launch asks for the device's resident capacity, so only a
+ * kernel on another stream that holds CUs for longer than the wait bound can
+ * make a wait give up.  Other T <= 4 cases run in four to six launches
  * (T <= 8 when no grouped-GEMM kernel serves the formats); larger T runs the
  * dispatch + grouped-GEMM path (or the GEMV path for formats it lacks). */
 moe_status moe_forward(const moe_config* cfg /*host*/, const uint16_t* x, int32_t T,

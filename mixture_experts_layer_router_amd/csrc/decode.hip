@@ -27,13 +27,21 @@
 // logits); DN needs the routing for its weight addresses and SU + RG for h.
 // A DN item issues its weight loads first and only then waits for h, so the
 // down weights stream while the last gate/up items finish.  Item i sits in
-// queue i % kQ; workgroup b takes the items of queue b % kQ in order with one
-// atomic each.  An item waits only for the router rows (which wait for
-// nothing) or for earlier items, and a queue hands out its items in order, so
-// the earliest unfinished item is always held by a running workgroup or about
-// to be taken by one: the launch completes whatever the number of resident
-// workgroups (at least max(E, kQ): the router rows' workgroups are the first
-// dispatched).
+// queue i % kQ.  With at most 16 items per workgroup (1 to 4 tokens) the
+// schedule is static: the j-th workgroup of queue q (workgroup b = q + kQ j)
+// takes the queue's items j, j + nq, j + 2 nq, ... (nq workgroups per queue)
+// in order; one device-scope atomic claim per item cost 2.7 us more per B=1
+// layer (48.1 against 45.4 us).  With more items (8 tokens: about 26 per
+// workgroup) the round robin balances worse than claims (240 against 235 us),
+// so workgroup b claims the items of queue q in order with one atomic each.
+// An item waits only for the router rows (which wait for nothing) or for
+// earlier items, and every workgroup takes its items in increasing order, so
+// the earliest unfinished item always belongs to a workgroup that can run
+// it.  Static: the launch completes once all its workgroups have been
+// resident; claims: once max(E, kQ) of them are resident at a time (the
+// router rows' workgroups are the first dispatched, and each queue needs a
+// server).  The grid is the device's resident capacity, so either holds
+// unless a kernel on another stream keeps CUs busy beyond the waits' bound.
 //
 // Same-address device-scope atomics serialise at about 12 ns each, so a
 // workgroup counts its finished items of a phase in a register and adds them
@@ -72,7 +80,7 @@ constexpr int kPhases = 2;     // phases that signal completion: SU, RG
 constexpr uint64_t kWaitTicks = 20000000;  // s_memrealtime runs at 100 MHz: 0.2 s
 
 // Counter block (one counter per 128-byte line, word 0 of the line):
-//   line 0: error word, epoch word         lines 1..kQ: queue heads
+//   line 0: error word, epoch word         lines 1..kQ: queue heads (dynamic schedule)
 //   per phase f: stripe summary, ready flag
 //   exit stripes (kQ) and exit summary
 //   per phase f: item counters of the kQ stripes
@@ -436,21 +444,24 @@ __global__ __launch_bounds__(256, 3) void fused_decode_kernel(FusedDecodeParams 
   // R: workgroup e < E computes router row e before it joins the queues (the
   // lowest block indices are dispatched first, so the routing, which every
   // routed item waits for, starts at once)
-  if (int(blockIdx.x) < E) {
-    if (tid == 0) s_next = q + kQ * atomic_inc(c.head(q));
+  // static schedule: workgroup b is the (b / kQ)-th of queue q's nq
+  // workgroups and takes the queue's items b / kQ + nq r, r = 0, 1, ...;
+  // dynamic: it claims them (the first claim before its router row)
+  const unsigned nq = unsigned(int(gridDim.x) / kQ + (q < int(gridDim.x) % kQ));
+  const bool stat = total <= 16u * unsigned(gridDim.x);
+  if (!stat && tid == 0) s_next = q + kQ * atomic_inc(c.head(q));
+  if (int(blockIdx.x) < E)
     router_row<MAXT>(d.x, T, d.wr, d.rp, blockIdx.x, nullptr, part, false, XG ? nullptr : sx, c.tagged(), tag);
-  } else if (tid == 0) {
-    s_next = q + kQ * atomic_inc(c.head(q));
-  }
   __syncthreads();
-  unsigned item = s_next, next = 0;
-  __syncthreads();  // thread 0 writes s_next again (first item) only after every thread has read it
+  unsigned item = stat ? blockIdx.x : s_next, next = 0, round = 0;
+  __syncthreads();  // thread 0 writes s_next again only after every thread has read it
   while (item < total) {
-    // claim the next item now; thread 0 hands it to the workgroup (s_next)
-    // once this item's loads are consumed and before its stores are issued:
-    // stores share the counter that the wait for the claim's value uses, so
-    // a later hand-over would also wait for the stores to complete
-    if (tid == 0) next = atomic_inc(c.head(q));
+    // the next item (claimed now); thread 0 hands it to the workgroup
+    // (s_next) once this item's loads are consumed and before its stores are
+    // issued: stores share the counter that the wait for the claim's value
+    // uses, so a later hand-over would also wait for the stores to complete
+    ++round;
+    if (tid == 0) next = stat ? blockIdx.x / kQ + nq * round : atomic_inc(c.head(q));
     auto hand_over = [&] {
       if (tid == 0) s_next = q + kQ * next;
     };
