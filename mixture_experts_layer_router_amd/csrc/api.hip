@@ -313,14 +313,15 @@ moe_status route_dispatch(const moe_config* c, const uint16_t* h, int T, const N
 // GEMM-path FFN on rows already laid out per segment (or all rows for the
 // shared expert).  A: activation rows in `afmt` (bf16 when A_NONE); a_map
 // gathers rows.  Output: y (fp32 or bf16) [rows][H].
-moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void* As, const int* a_map, int a_div,
-                    int rows, const int* seg, const int* tiles, const int* ntiles, int maxt, int bm,
-                    const moe_ffn_weights* W, void* h, void* hs, void* y, bool y_bf16, hipStream_t s) {
+// The two GEMMs of an expert FFN: gate/up (with SiLU * up and h in the
+// activation format) into h, and down from h into y.
+void ffn_gemm_params(const moe_config* c, bool routed, const void* A, const void* As, const int* a_map, int a_div,
+                     int rows, const int* seg, const int* tiles, const int* ntiles, int maxt, int bm,
+                     const moe_ffn_weights* W, void* h, void* hs, void* y, GemmParams* gp, GemmParams* dp) {
   const int wf = routed ? c->routed_wfmt : c->shared_wfmt;
   const int af = routed ? c->routed_afmt : c->shared_afmt;
   const int I = routed ? c->inter : c->shared_inter;
   const int H = c->hidden;
-  hipStream_t s_ = s;
   GemmParams g{};
   g.A = A;
   g.lda = H;
@@ -345,7 +346,6 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   g.ldc = I;
   g.Cs = hs;
   g.out_afmt = af;
-  LAUNCH(routed ? "gemm_gate_up_routed" : "gemm_gate_up_shared", launch_gemm(wf, EPI_GATEUP, g, s));
   GemmParams d{};
   d.A = h;
   d.lda = I;
@@ -364,6 +364,18 @@ moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void*
   d.bm = bm;
   d.C = y;
   d.ldc = H;
+  *gp = g;
+  *dp = d;
+}
+
+moe_status gemm_ffn(const moe_config* c, bool routed, const void* A, const void* As, const int* a_map, int a_div,
+                    int rows, const int* seg, const int* tiles, const int* ntiles, int maxt, int bm,
+                    const moe_ffn_weights* W, void* h, void* hs, void* y, bool y_bf16, hipStream_t s) {
+  const int wf = routed ? c->routed_wfmt : c->shared_wfmt;
+  hipStream_t s_ = s;
+  GemmParams g, d;
+  ffn_gemm_params(c, routed, A, As, a_map, a_div, rows, seg, tiles, ntiles, maxt, bm, W, h, hs, y, &g, &d);
+  LAUNCH(routed ? "gemm_gate_up_routed" : "gemm_gate_up_shared", launch_gemm(wf, EPI_GATEUP, g, s));
   LAUNCH(routed ? "gemm_down_routed" : "gemm_down_shared", launch_gemm(wf, y_bf16 ? EPI_BF16 : EPI_F32, d, s));
   return MOE_OK;
 }
@@ -671,28 +683,45 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* x, int32_t T, con
     xa = at<void>(ws, L.xq);
     xas = at<void>(ws, L.xqs);
   }
-  if ((st = gemm_ffn(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, rbm), rbm, routed,
-                     at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), true, stream)) != MOE_OK)
-    return st;
-  if (has_shared && !side) {  // in order on the caller's stream
-    const void* xs = xin;
-    const void* xss = nullptr;
-    if (saf != A_NONE) {
-      if (saf == raf) {
-        xs = xa;
-        xss = xas;
-      } else {
-        LAUNCH("quant_rows", launch_quant_rows(xin, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
-                                  nullptr, stream));
-        xs = at<void>(ws, L.xs2);
-        xss = at<void>(ws, L.xs2s);
-      }
+  // shared expert in order on the caller's stream: its input
+  const void* xs = xin;
+  const void* xss = nullptr;
+  if (has_shared && !side && saf != A_NONE) {
+    if (saf == raf) {
+      xs = xa;
+      xss = xas;
+    } else {
+      LAUNCH("quant_rows", launch_quant_rows(xin, false, T, H, nullptr, 1, saf, at<void>(ws, L.xs2), at<void>(ws, L.xs2s),
+                                nullptr, stream));
+      xs = at<void>(ws, L.xs2);
+      xss = at<void>(ws, L.xs2s);
     }
+  }
+  GemmParams rg, rd, sgp, sdp;
+  ffn_gemm_params(cfg, true, xa, xas, perm, K, TK, off, tiles, ntiles, max_tiles(TK, E, rbm), rbm, routed,
+                  at<void>(ws, L.h), at<void>(ws, L.hs), at<void>(ws, L.yperm), &rg, &rd);
+  if (has_shared && !side) {
     ysh = at<float>(ws, L.ysh);
-    if ((st = gemm_ffn(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
-                       ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
-                       at<void>(ws, L.hshs), ysh, true, stream)) != MOE_OK)
-      return st;
+    ffn_gemm_params(cfg, false, xs, xss, nullptr, 1, T, nullptr, nullptr, nullptr, 0,
+                    ffn_tile_rows(cfg->shared_wfmt, H, cfg->shared_inter), shared, at<void>(ws, L.hsh),
+                    at<void>(ws, L.hshs), ysh, &sgp, &sdp);
+  }
+  // Both down GEMMs on the large-tile kernel (the 2,048-token MXFP8 layer:
+  // 3.5 waves of routed tiles, 0.875 of shared ones): one launch, the
+  // shared tiles first, so each GEMM's partial last wave is filled with the
+  // other's tiles.
+  const int swf = cfg->shared_wfmt, rwf = cfg->routed_wfmt;
+  const bool dual = has_shared && !side && gemm2_chosen(rwf, EPI_BF16, rd) && gemm2_chosen(swf, EPI_BF16, sdp);
+  LAUNCH("gemm_gate_up_routed", launch_gemm(rwf, EPI_GATEUP, rg, stream));
+  if (dual) {
+    LAUNCH("gemm_gate_up_shared", launch_gemm(swf, EPI_GATEUP, sgp, stream));
+    LAUNCH("gemm_down_shared_routed", launch_gemm2_dual(swf, sdp, rwf, rd, stream));
+  } else {
+    LAUNCH("gemm_down_routed", launch_gemm(rwf, EPI_BF16, rd, stream));
+    if (has_shared && !side) {
+      LAUNCH("gemm_gate_up_shared", launch_gemm(swf, EPI_GATEUP, sgp, stream));
+      LAUNCH("gemm_down_shared", launch_gemm(swf, EPI_BF16, sdp, stream));
+    }
   }
   HIP_TRY(joiner.join());
   // Y_perm and the shared output are bf16 here (the combine sums in fp32 and rounds once)

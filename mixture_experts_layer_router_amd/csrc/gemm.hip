@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   const int nper = EPI == EPI_GATEUP ? BNT / 2 : BNT;  // output columns per tile
   const int KS = (EPI == EPI_F32 && p.ksplit > 1) ? p.ksplit : 1;
-  const Tile tl = tile_of(p, BM, nper, KS);
+  const Tile tl = tile_of(p, BM, nper, KS, int(blockIdx.x));
   if (!tl.valid) return;
   const int e = tl.e, m0 = tl.m0, n0 = tl.n0, seg0 = tl.seg0, mrows = tl.mrows, kz = tl.kz;
   const int K = p.K;

@@ -93,13 +93,21 @@ struct Single {
   uint32_t sb[3], sax;
 };
 
+// LDS of one workgroup: the operand buffers, then (MXFP8) the scale buffers
+// of A (288 rows and 32 rows of room for the extra rows' 64-lane load) and B
+constexpr int kLdsOps = kBufs * (kLdsA + kLdsB);
+constexpr int kLdsSA = kSBuf * (BMX + 32) * 16;
+constexpr int kLdsSB = kSBuf * BNT * 16;
+constexpr int kLdsAll = kLdsOps + kLdsSA + kLdsSB;
+
+// One workgroup's tile of the GEMM p; bid is its index among p's workgroups
+// (see tile_of), lds its kLdsAll bytes of LDS (1 KB aligned).
 template <int WF, int EPI>
-__global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
+MOE_DEV void gemm2_body(const GemmParams& p, uint8_t* lds, int bid) {
   constexpr bool MX = WF == W_MXFP8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * (kLdsA + kLdsB)];
-  // MX scales: A rows (288, and 32 rows of room for the extra rows' 64-lane load) and B rows
-  __shared__ __attribute__((aligned(16))) uint8_t sSA[MX ? kSBuf : 1][MX ? (BMX + 32) * 16 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sSB[MX ? kSBuf : 1][MX ? BNT * 16 : 16];
+  uint8_t* const smem = lds;
+  auto& sSA = *reinterpret_cast<uint8_t(*)[kSBuf][(BMX + 32) * 16]>(lds + kLdsOps);
+  auto& sSB = *reinterpret_cast<uint8_t(*)[kSBuf][BNT * 16]>(lds + kLdsOps + kLdsSA);
 
 
   const int tid = threadIdx.x;
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   int g = lane >> 5, l32 = lane & 31;
   constexpr int nper = EPI == EPI_GATEUP ? BNT / 2 : BNT;  // output columns per tile
   const int KS = (EPI == EPI_F32 && p.ksplit > 1) ? p.ksplit : 1;
-  const Tile tl = tile_of(p, BM, nper, KS);
+  const Tile tl = tile_of(p, BM, nper, KS, bid);
   if (!tl.valid) return;
   const int e = tl.e, m0 = tl.m0, n0 = tl.n0, seg0 = tl.seg0, mrows = tl.mrows, kz = tl.kz;
   const int K = p.K, N = p.N;
@@ -555,6 +563,25 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
   }
 }
 
+template <int WF, int EPI>
+__global__ __launch_bounds__(256) void gemm2_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsAll];
+  gemm2_body<WF, EPI>(p, lds, int(blockIdx.x));
+}
+
+// Two GEMMs in one launch: workgroups [0, n1) run p1, the rest p2 (n1 is a
+// multiple of 8, so both keep their XCD-aware tile order).  A GEMM whose
+// tiles leave part of the last wave idle then shares that wave with the
+// other's tiles instead of running after it.
+template <int WF1, int EPI1, int WF2, int EPI2>
+__global__ __launch_bounds__(256) void gemm2_dual_kernel(GemmParams p1, int n1, GemmParams p2) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsAll];
+  if (int(blockIdx.x) < n1)
+    gemm2_body<WF1, EPI1>(p1, lds, int(blockIdx.x));
+  else
+    gemm2_body<WF2, EPI2>(p2, lds, int(blockIdx.x) - n1);
+}
+
 template <int WF>
 hipError_t launch_epi(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
   switch (epi) {
@@ -566,6 +593,33 @@ hipError_t launch_epi(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm2_dual(int wf1, const GemmParams& p1, int wf2, const GemmParams& p2, hipStream_t s) {
+  auto tiles_of = [](int wf, const GemmParams& p) -> long {
+    const int ntile = p.tiles ? p.max_tiles : (p.M + BM - 1) / BM;
+    if (ntile <= 0) return 0;
+    const long es = wf == W_BF16 ? 2 : 1;
+    const long a_rows = p.a_map ? (long(p.M) + p.a_div - 1) / p.a_div : long(p.M);
+    if (a_rows * p.lda * es >= (1L << 32) || long(p.N) * p.K * es >= (1L << 32)) return -1;
+    return (long(ntile) * ((p.N + BNT - 1) / BNT) + 7) / 8 * 8;
+  };
+  if (!gemm2_serves(wf1, p1.K, EPI_BF16, A_NONE, p1.ksplit) || !gemm2_serves(wf2, p2.K, EPI_BF16, A_NONE, p2.ksplit))
+    return hipErrorInvalidValue;
+  const long n1 = tiles_of(wf1, p1), n2 = tiles_of(wf2, p2);
+  if (n1 < 0 || n2 < 0) return hipErrorInvalidValue;
+  if (n1 + n2 == 0) return hipSuccess;
+  const dim3 grid(unsigned(n1 + n2));
+  const int n1i = int(n1);
+  if (wf1 == W_BF16 && wf2 == W_MXFP8)
+    hipLaunchKernelGGL((gemm2_dual_kernel<W_BF16, EPI_BF16, W_MXFP8, EPI_BF16>), grid, dim3(256), 0, s, p1, n1i, p2);
+  else if (wf1 == W_MXFP8 && wf2 == W_MXFP8)
+    hipLaunchKernelGGL((gemm2_dual_kernel<W_MXFP8, EPI_BF16, W_MXFP8, EPI_BF16>), grid, dim3(256), 0, s, p1, n1i, p2);
+  else if (wf1 == W_BF16 && wf2 == W_BF16)
+    hipLaunchKernelGGL((gemm2_dual_kernel<W_BF16, EPI_BF16, W_BF16, EPI_BF16>), grid, dim3(256), 0, s, p1, n1i, p2);
+  else
+    hipLaunchKernelGGL((gemm2_dual_kernel<W_MXFP8, EPI_BF16, W_BF16, EPI_BF16>), grid, dim3(256), 0, s, p1, n1i, p2);
+  return hipGetLastError();
+}
 
 bool gemm2_serves(int wfmt, int K, int epi, int out_afmt, int ksplit) {
   if (wfmt == W_BF16) return K % 64 == 0 && (epi != EPI_GATEUP || out_afmt == A_NONE);

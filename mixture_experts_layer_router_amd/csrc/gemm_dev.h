@@ -64,14 +64,17 @@ struct Tile {
   int e, m0, n0, kz, seg0, mrows;
   bool valid;
 };
-MOE_DEV Tile tile_of(const GemmParams& p, int bm, int nper, int ks) {
+// bid: the workgroup's index among the launch's workgroups of this GEMM
+// (blockIdx.x, or its offset in a launch shared with another GEMM, which
+// keeps bid % 8 = blockIdx.x % 8 when that offset is a multiple of 8).
+MOE_DEV Tile tile_of(const GemmParams& p, int bm, int nper, int ks, int bid) {
   Tile t{};
   const int NB = (p.N + nper - 1) / nper;
   const int nt_list = p.tiles ? p.ntiles[0] : (p.M + bm - 1) / bm;
   const int T = nt_list * NB * ks;
   const int chunk = (T + 7) / 8;
-  int idx = int(blockIdx.x % 8) * chunk + int(blockIdx.x / 8);
-  if (int(blockIdx.x / 8) >= chunk || idx >= T) return t;
+  int idx = (bid % 8) * chunk + bid / 8;
+  if (bid / 8 >= chunk || idx >= T) return t;
   t.kz = idx % ks;  // K slice (split-K: slices of one tile are adjacent)
   idx /= ks;
   int e = 0, nb, m0, step = bm;

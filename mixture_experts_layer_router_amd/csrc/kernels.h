@@ -181,6 +181,9 @@ bool gemm2_serves(int wfmt, int K, int epi, int out_afmt, int ksplit);
 // its tiles still fill the chip
 bool gemm2_chosen(int wfmt, int epi, const GemmParams& p);
 hipError_t launch_gemm2(int wfmt, int epi, const GemmParams& p, hipStream_t s);
+// two bf16-output GEMMs of the large-tile kernel in one launch, p1's tiles
+// first (both must be ones gemm2_chosen picks)
+hipError_t launch_gemm2_dual(int wf1, const GemmParams& p1, int wf2, const GemmParams& p2, hipStream_t s);
 // rows per tile of an expert FFN's two GEMMs (gate/up with K = H, down with K = I)
 inline int ffn_tile_rows(int wfmt, int H, int I) {
   return (wfmt == W_BF16 || (wfmt == W_MXFP8 && H % 512 == 0 && I % 512 == 0)) ? kGemm2BM : kGemmBM;
