@@ -93,15 +93,22 @@ NORM_LAYERS = {
 }
 
 
-@pytest.mark.parametrize("path", ["auto", "staged", "gemv", "gemm"])
-@pytest.mark.parametrize("name", list(NORM_LAYERS))
+# the format pairs the GEMM path has kernels for
+GEMM_PAIRS = {("bf16", "none"), ("fp8_b128", "fp8_1x128"), ("mxfp8", "mxfp8_1x32")}
+
+
+def served(cfg, path):
+    """Whether the library has the forced path for cfg: no GEMM kernel for
+    some format pairs, and the staged small-T path serves T <= 8."""
+    if path == "gemm":
+        return (cfg.routed_wfmt, cfg.routed_afmt) in GEMM_PAIRS and (cfg.shared_wfmt, cfg.shared_afmt) in GEMM_PAIRS
+    return path != "staged" or cfg.tokens <= 8
+
+
+@pytest.mark.parametrize("name,path", [(n, p) for n in NORM_LAYERS for p in ["auto", "staged", "gemv", "gemm"]
+                                       if served(NORM_LAYERS[n], p)])
 def test_forward_norm_small(name, path, monkeypatch):
     cfg = NORM_LAYERS[name]
-    ok = {("bf16", "none"), ("fp8_b128", "fp8_1x128"), ("mxfp8", "mxfp8_1x32")}
-    if path == "gemm" and ((cfg.routed_wfmt, cfg.routed_afmt) not in ok or (cfg.shared_wfmt, cfg.shared_afmt) not in ok):
-        pytest.skip("no GEMM kernel for this format pair")
-    if path == "staged" and cfg.tokens > 8:
-        pytest.skip("the staged small-T path serves T <= 8")
     if path != "auto":
         monkeypatch.setenv("MOE_FORCE_PATH", path)
     say(f"[forward_norm] {name} {path}")
